@@ -1,0 +1,297 @@
+/*
+ * qmm_oracle.c -- plain CPU oracle for the weight-only quantized matmul.
+ *
+ * TEST INFRASTRUCTURE ONLY (see qmm_oracle.h): used by the tests, the smoke
+ * check and the benchmark's CPU baseline, never by the product path.
+ *
+ * Sources of each step (pages are cited by project, file and passage):
+ *  - canonical packing and unpack rule: BitDistiller, quantization/
+ *    triton_kernels.py, quant_matmul_kernel -- operand shapes in its
+ *    docstring, the per-element shifter (k mod pack_num) * w_bit and the
+ *    "(packed >> shifter) & offset" unpack;
+ *  - group index floor(k / group_size): same kernel, scale-loading step
+ *    (k_iters_per_quant_group / grp_idx);
+ *  - dequant w = (q - z) * s with an integer zero point, and the symmetric
+ *    zero 8 for int4: aphrodite-engine marlin_cuda_kernel.cu, dequant()
+ *    (the "-8 symmetric zero point" fused into its SUB/ADD constants);
+ *  - int8 per-row scale applied after the sum over k, fp32 accumulation:
+ *    tiny-llm src/tinyllm/kernels/int8_gemv.py, module docstring and
+ *    int8_matmul() docstring.
+ *
+ * Readings where the pages are silent (the zero-point packing rule, the
+ * symmetric zero for int2) are listed in the project design notes.
+ */
+#include "qmm_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* c1: 16-bit float decodes, from the format definitions              */
+/* ------------------------------------------------------------------ */
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
+ * bits.  Exponent field 0 encodes zero and subnormals (fraction * 2^-24),
+ * field 31 encodes infinities (fraction 0) and NaNs. */
+float orc_f16_to_f32(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -24);
+    } else if (e == 31) {
+        v = (f == 0) ? INFINITY : NAN;
+    } else {
+        v = ldexp((double)(1024 + f), e - 25); /* (1 + f/1024) * 2^(e-15) */
+    }
+    return (float)(sign ? -v : v);
+}
+
+/* bfloat16 is by definition the upper 16 bits of an IEEE binary32 word. */
+float orc_bf16_to_f32(uint16_t h) {
+    uint32_t bits = (uint32_t)h << 16;
+    float v;
+    memcpy(&v, &bits, sizeof v);
+    return v;
+}
+
+void orc_f16_to_f32_n(const uint16_t* h, float* out, size_t n) {
+    for (size_t i = 0; i < n; ++i) out[i] = orc_f16_to_f32(h[i]);
+}
+
+void orc_bf16_to_f32_n(const uint16_t* h, float* out, size_t n) {
+    for (size_t i = 0; i < n; ++i) out[i] = orc_bf16_to_f32(h[i]);
+}
+
+static double x_at(const uint16_t* x, int x_dtype, int K, int m, int k) {
+    uint16_t h = x[(size_t)m * K + k];
+    return (double)(x_dtype == 0 ? orc_f16_to_f32(h) : orc_bf16_to_f32(h));
+}
+
+/* ------------------------------------------------------------------ */
+/* argument checks                                                     */
+/* ------------------------------------------------------------------ */
+
+static int check_lowbit(int N, int K, int w_bit, int group_size) {
+    if (N < 0 || K < 0) return -1;
+    if (w_bit != 2 && w_bit != 4) return -1;
+    if (group_size <= 0) return -1;
+    if (K % group_size != 0) return -1;
+    if (K % (32 / w_bit) != 0) return -1;
+    return 0;
+}
+
+static int check_args(int N, int K, int w_bit, int group_size, const int32_t* zeros) {
+    if (w_bit == 8) {
+        if (N < 0 || K < 0 || group_size != 0 || zeros != NULL) return -1;
+        return 0;
+    }
+    return check_lowbit(N, K, w_bit, group_size);
+}
+
+/* ------------------------------------------------------------------ */
+/* c2/c3: unpack                                                       */
+/* ------------------------------------------------------------------ */
+
+/* Element k of column n sits in word k / pack of that column, at bit
+ * (k mod pack) * w_bit, least significant first; the mask is 2^w_bit - 1
+ * (BitDistiller quant_matmul_kernel: weight-load and unpack step). */
+uint32_t orc_q_at(const int32_t* qw, int N, int w_bit, int k, int n) {
+    int pack = 32 / w_bit;
+    uint32_t word = (uint32_t)qw[(size_t)(k / pack) * N + n];
+    return (word >> ((k % pack) * w_bit)) & ((1u << w_bit) - 1u);
+}
+
+/* Zero points are packed the same way along the group axis; without zeros
+ * the symmetric midpoint 2^(w_bit-1) is used (8 for int4, as in Marlin's
+ * dequant()). */
+uint32_t orc_z_at(const int32_t* qz, int N, int w_bit, int g, int n) {
+    if (qz == NULL) return 1u << (w_bit - 1);
+    int pack = 32 / w_bit;
+    uint32_t word = (uint32_t)qz[(size_t)(g / pack) * N + n];
+    return (word >> ((g % pack) * w_bit)) & ((1u << w_bit) - 1u);
+}
+
+int orc_unpack_q(const int32_t* qw, int N, int K, int w_bit, uint8_t* q_out) {
+    if (N < 0 || K < 0 || (w_bit != 2 && w_bit != 4) || K % (32 / w_bit)) return -1;
+    for (int k = 0; k < K; ++k)
+        for (int n = 0; n < N; ++n)
+            q_out[(size_t)k * N + n] = (uint8_t)orc_q_at(qw, N, w_bit, k, n);
+    return 0;
+}
+
+int orc_unpack_z(const int32_t* qz, int N, int G, int w_bit, uint8_t* z_out) {
+    if (N < 0 || G < 0 || (w_bit != 2 && w_bit != 4)) return -1;
+    for (int g = 0; g < G; ++g)
+        for (int n = 0; n < N; ++n)
+            z_out[(size_t)g * N + n] = (uint8_t)orc_z_at(qz, N, w_bit, g, n);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* c4: dequant                                                         */
+/* ------------------------------------------------------------------ */
+
+/* w = (q - z) * s, s the fp16 scale of group floor(k / group_size).
+ * |q - z| <= 15 needs 4 bits and s has an 11-bit significand, so the fp32
+ * product is exact.  int8: w = q exactly (|q| <= 128); the fp32 row scale
+ * is applied after the sum (tiny-llm int8_gemv.py docstring). */
+float orc_w_at(const void* Q, const void* scales, const int32_t* zeros,
+               int N, int K, int w_bit, int group_size, int k, int n) {
+    if (w_bit == 8) {
+        const int8_t* q8 = (const int8_t*)Q;
+        return (float)q8[(size_t)n * K + k];
+    }
+    int g = k / group_size;
+    int q = (int)orc_q_at((const int32_t*)Q, N, w_bit, k, n);
+    int z = (int)orc_z_at(zeros, N, w_bit, g, n);
+    float s = orc_f16_to_f32(((const uint16_t*)scales)[(size_t)g * N + n]);
+    return (float)(q - z) * s;
+}
+
+int orc_dequant(const void* Q, const void* scales, const int32_t* zeros,
+                int N, int K, int w_bit, int group_size, float* w_out) {
+    if (check_args(N, K, w_bit, group_size, zeros)) return -1;
+    for (int k = 0; k < K; ++k)
+        for (int n = 0; n < N; ++n)
+            w_out[(size_t)k * N + n] =
+                orc_w_at(Q, scales, zeros, N, K, w_bit, group_size, k, n);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* c5: the product, fp64 accumulation, k ascending                     */
+/* ------------------------------------------------------------------ */
+
+static double row_scale(const void* scales, int w_bit, int n) {
+    return w_bit == 8 ? (double)((const float*)scales)[n] : 1.0;
+}
+
+int orc_qmm(const uint16_t* x, int x_dtype, const void* Q, const void* scales,
+            const int32_t* zeros, int M, int N, int K, int w_bit, int group_size,
+            double* y_ref, double* abs_ref) {
+    if (M < 0 || (x_dtype != 0 && x_dtype != 1)) return -1;
+    if (check_args(N, K, w_bit, group_size, zeros)) return -1;
+    /* Dequantize once into column-major storage wt[n][k] (storage order only). */
+    float* wt = (float*)malloc(sizeof(float) * ((size_t)N * K + 1));
+    double* xr = (double*)malloc(sizeof(double) * ((size_t)K + 1));
+    if (!wt || !xr) { free(wt); free(xr); return -1; }
+    for (int n = 0; n < N; ++n)
+        for (int k = 0; k < K; ++k)
+            wt[(size_t)n * K + k] = orc_w_at(Q, scales, zeros, N, K, w_bit, group_size, k, n);
+    for (int m = 0; m < M; ++m) {
+        for (int k = 0; k < K; ++k) xr[k] = x_at(x, x_dtype, K, m, k);
+        for (int n = 0; n < N; ++n) {
+            const float* w = wt + (size_t)n * K;
+            double s = row_scale(scales, w_bit, n);
+            double acc = 0.0, ab = 0.0;
+            for (int k = 0; k < K; ++k) {
+                double p = xr[k] * (double)w[k];
+                acc += p;
+                ab += fabs(p * s);
+            }
+            y_ref[(size_t)m * N + n] = s * acc;
+            abs_ref[(size_t)m * N + n] = ab;
+        }
+    }
+    free(wt);
+    free(xr);
+    return 0;
+}
+
+int orc_qmm_at(const uint16_t* x, int x_dtype, const void* Q, const void* scales,
+               const int32_t* zeros, int M, int N, int K, int w_bit, int group_size,
+               int count, const int* ms, const int* ns, double* y_ref, double* abs_ref) {
+    if (M < 0 || count < 0 || (x_dtype != 0 && x_dtype != 1)) return -1;
+    if (check_args(N, K, w_bit, group_size, zeros)) return -1;
+    for (int i = 0; i < count; ++i) {
+        int m = ms[i], n = ns[i];
+        if (m < 0 || m >= M || n < 0 || n >= N) return -1;
+        double s = row_scale(scales, w_bit, n);
+        double acc = 0.0, ab = 0.0;
+        for (int k = 0; k < K; ++k) {
+            double p = x_at(x, x_dtype, K, m, k) *
+                       (double)orc_w_at(Q, scales, zeros, N, K, w_bit, group_size, k, n);
+            acc += p;
+            ab += fabs(p * s);
+        }
+        y_ref[i] = s * acc;
+        abs_ref[i] = ab;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* MFMA tile layout: reference permutation from the layout spec        */
+/* ------------------------------------------------------------------ */
+/*
+ * The layout is this project's own (the pages print no repack routine).
+ * Columns are taken in strips of 16; K in blocks of KB = 128 (int4),
+ * 256 (int2) or 64 (int8).  Each (strip s, K-block kb) is one contiguous
+ * 1024-byte block, blocks ordered strip-major: b = s * (K / KB) + kb.
+ * Inside a block, "lane" L in [0, 64) owns bytes [16 L, 16 L + 16); it
+ * serves column n = 16 s + (L mod 16) and k-octet c = L / 16.
+ *   int4: word j (0..3) of lane L holds k = 128 kb + 32 j + 8 c + i,
+ *         i = 0..7, in nibble slot i/2 (i even) or 4 + i/2 (i odd).
+ *   int2: word j of lane L holds k = 256 kb + 64 j + 32 h + 8 c + i,
+ *         h = 0..1, i = 0..7, in 2-bit slot 4 h + i/2 (i even) or
+ *         8 + 4 h + i/2 (i odd).
+ *   int8: byte 8 h + i of lane L holds k = 64 kb + 32 h + 8 c + i.
+ */
+static int mfma_kb(int w_bit) { return w_bit == 4 ? 128 : (w_bit == 2 ? 256 : 64); }
+
+size_t orc_mfma_bytes(int N, int K, int w_bit) {
+    if (w_bit != 2 && w_bit != 4 && w_bit != 8) return 0;
+    if (N < 0 || K < 0 || N % 16 || K % mfma_kb(w_bit)) return 0;
+    return (size_t)N * K * w_bit / 8;
+}
+
+int orc_mfma_locate(int N, int K, int w_bit, int k, int n, size_t* where, int* shift) {
+    if (orc_mfma_bytes(N, K, w_bit) == 0 && (N * (size_t)K) != 0) return -1;
+    if (k < 0 || k >= K || n < 0 || n >= N) return -1;
+    int KB = mfma_kb(w_bit);
+    int s = n / 16, kb = k / KB, r = k % KB;
+    size_t block = (size_t)s * (K / KB) + kb;
+    int col = n % 16;
+    if (w_bit == 4) {
+        int j = r / 32, c = (r % 32) / 8, i = r % 8;
+        int lane = 16 * c + col;
+        int slot = (i % 2 == 0) ? i / 2 : 4 + i / 2;
+        *where = block * 256 + (size_t)lane * 4 + j; /* int32 word index */
+        *shift = 4 * slot;
+    } else if (w_bit == 2) {
+        int j = r / 64, h = (r % 64) / 32, c = (r % 32) / 8, i = r % 8;
+        int lane = 16 * c + col;
+        int slot = (i % 2 == 0) ? 4 * h + i / 2 : 8 + 4 * h + i / 2;
+        *where = block * 256 + (size_t)lane * 4 + j;
+        *shift = 2 * slot;
+    } else {
+        int h = r / 32, c = (r % 32) / 8, i = r % 8;
+        int lane = 16 * c + col;
+        *where = block * 1024 + (size_t)lane * 16 + 8 * h + i; /* byte index */
+        *shift = 0;
+    }
+    return 0;
+}
+
+int orc_mfma_pack(const void* Q_canon, void* Q_mfma, int N, int K, int w_bit) {
+    size_t bytes = orc_mfma_bytes(N, K, w_bit);
+    if (bytes == 0 && (size_t)N * K != 0) return -1;
+    memset(Q_mfma, 0, bytes);
+    for (int k = 0; k < K; ++k) {
+        for (int n = 0; n < N; ++n) {
+            size_t where;
+            int shift;
+            orc_mfma_locate(N, K, w_bit, k, n, &where, &shift);
+            if (w_bit == 8) {
+                ((int8_t*)Q_mfma)[where] = ((const int8_t*)Q_canon)[(size_t)n * K + k];
+            } else {
+                uint32_t q = orc_q_at((const int32_t*)Q_canon, N, w_bit, k, n);
+                ((uint32_t*)Q_mfma)[where] |= q << shift;
+            }
+        }
+    }
+    return 0;
+}

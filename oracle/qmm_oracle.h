@@ -1,0 +1,73 @@
+/*
+ * qmm_oracle.h -- CPU oracle for the weight-only quantized matmul
+ *
+ *     y[m][n] = sum_k x[m][k] * W[k][n],   W = dequant(Q)
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path links, loads or
+ * calls this library: only the tests, the package smoke check and the
+ * benchmark's CPU-baseline leg do.  It shares no code, header, table or
+ * constant with the HIP library.
+ *
+ * Plain, slow, single-threaded C99.  Every decode is written from its
+ * definition; the matmul accumulates in fp64 with k ascending.
+ *
+ * Operand conventions (all arrays contiguous, row-major):
+ *   x       (M, K) 16-bit words, fp16 (x_dtype 0) or bf16 (x_dtype 1)
+ *   w_bit 2|4: Q = qw (K/pack, N) int32, pack = 32/w_bit;
+ *              scales (K/group_size, N) fp16 bit patterns;
+ *              zeros  NULL (symmetric, z = 2^(w_bit-1)) or
+ *                     (ceil(G/pack), N) int32 packed along the group axis
+ *   w_bit 8:   Q (N, K) int8; scales (N,) fp32; zeros NULL; group_size 0
+ * Return codes: 0 ok, -1 bad argument.
+ */
+#ifndef QMM_ORACLE_H
+#define QMM_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+float orc_f16_to_f32(uint16_t h);
+float orc_bf16_to_f32(uint16_t h);
+void orc_f16_to_f32_n(const uint16_t* h, float* out, size_t n);
+void orc_bf16_to_f32_n(const uint16_t* h, float* out, size_t n);
+
+/* Integer code of element (k, n) of a canonical low-bit weight. */
+uint32_t orc_q_at(const int32_t* qw, int N, int w_bit, int k, int n);
+/* Zero point of group g, column n (symmetric when qz == NULL). */
+uint32_t orc_z_at(const int32_t* qz, int N, int w_bit, int g, int n);
+
+/* Dequantized weight W[k][n] (fp32, exact).  int8: the raw code, scale not
+ * applied (it is applied after the sum). */
+float orc_w_at(const void* Q, const void* scales, const int32_t* zeros,
+               int N, int K, int w_bit, int group_size, int k, int n);
+
+/* Bulk unpack / dequant. */
+int orc_unpack_q(const int32_t* qw, int N, int K, int w_bit, uint8_t* q_out /*(K,N)*/);
+int orc_unpack_z(const int32_t* qz, int N, int G, int w_bit, uint8_t* z_out /*(G,N)*/);
+int orc_dequant(const void* Q, const void* scales, const int32_t* zeros,
+                int N, int K, int w_bit, int group_size, float* w_out /*(K,N)*/);
+
+/* Full product: y_ref and abs_ref = sum_k |x * w_eff| (M, N) in fp64. */
+int orc_qmm(const uint16_t* x, int x_dtype, const void* Q, const void* scales,
+            const int32_t* zeros, int M, int N, int K, int w_bit, int group_size,
+            double* y_ref, double* abs_ref);
+
+/* The same, for `count` chosen outputs (ms[i], ns[i]) only. */
+int orc_qmm_at(const uint16_t* x, int x_dtype, const void* Q, const void* scales,
+               const int32_t* zeros, int M, int N, int K, int w_bit, int group_size,
+               int count, const int* ms, const int* ns, double* y_ref, double* abs_ref);
+
+/* Reference permutation into the MFMA tile layout, written element by
+ * element from the layout specification (see orc_mfma_locate). */
+int orc_mfma_locate(int N, int K, int w_bit, int k, int n, size_t* byte_or_word, int* shift);
+size_t orc_mfma_bytes(int N, int K, int w_bit);
+int orc_mfma_pack(const void* Q_canon, void* Q_mfma, int N, int K, int w_bit);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
