@@ -1,0 +1,251 @@
+// qmm_api.cpp -- the C ABI (include/qmm.h): argument checks, launch plans,
+// dispatch onto the caller's stream.  Every check runs before the first HIP
+// call, so invalid calls are diagnosable on a machine without a GPU.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "../../include/qmm.h"
+#include "qmm_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+qmm_status fail(qmm_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+qmm_status ok() {
+  g_err[0] = '\0';
+  return QMM_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool group_supported(int g) { return g == 32 || g == 64 || g == 128 || g == 256; }
+
+// Checks shared by qmm_gemv, qmm_gemm and qmm_dequant on the operand table.
+// Sets *noop when a size is zero (after the enum / dtype checks).
+qmm_status check_operands(const char* fn, const void* Q, const void* scales, const void* zeros,
+                          int N, int K, int w_bit, int group_size, bool* noop) {
+  *noop = false;
+  if (N < 0 || K < 0) return fail(QMM_ERR_ARG, "%s: negative size N=%d K=%d", fn, N, K);
+  if (w_bit != 2 && w_bit != 4 && w_bit != 8)
+    return fail(QMM_ERR_ARG, "%s: w_bit must be 2, 4 or 8 (got %d)", fn, w_bit);
+  if (w_bit == 8) {
+    if (group_size != 0)
+      return fail(QMM_ERR_ARG, "%s: int8 uses a per-row scale; group_size must be 0 (got %d)",
+                  fn, group_size);
+    if (zeros != nullptr) return fail(QMM_ERR_ARG, "%s: int8 takes no zero points", fn);
+  } else {
+    if (group_size <= 0)
+      return fail(QMM_ERR_ARG, "%s: group_size must be positive (got %d)", fn, group_size);
+    if (K % group_size != 0)
+      return fail(QMM_ERR_ARG, "%s: K=%d is not a multiple of group_size=%d", fn, K, group_size);
+    if (!group_supported(group_size))
+      return fail(QMM_ERR_UNSUPPORTED, "%s: group_size %d not built (32, 64, 128, 256)", fn,
+                  group_size);
+  }
+  if (N == 0 || K == 0) {
+    *noop = true;
+    return QMM_OK;
+  }
+  if (Q == nullptr || scales == nullptr)
+    return fail(QMM_ERR_ARG, "%s: NULL Q or scales", fn);
+  if (!aligned16(Q) || !aligned16(scales) || !aligned16(zeros))
+    return fail(QMM_ERR_ARG, "%s: Q, scales and zeros must be 16-byte aligned", fn);
+  return QMM_OK;
+}
+
+qmm_status check_matmul(const char* fn, const void* x, const void* Q, const void* scales,
+                        const void* zeros, const float* y, int M, int N, int K, int w_bit,
+                        int group_size, int x_dtype, bool* noop) {
+  if (M < 0) return fail(QMM_ERR_ARG, "%s: negative M=%d", fn, M);
+  if (x_dtype != QMM_F16 && x_dtype != QMM_BF16)
+    return fail(QMM_ERR_ARG, "%s: x_dtype must be QMM_F16 or QMM_BF16 (got %d)", fn, x_dtype);
+  qmm_status st = check_operands(fn, Q, scales, zeros, N, K, w_bit, group_size, noop);
+  if (st != QMM_OK || *noop) return st;
+  if (M == 0) {
+    *noop = true;
+    return QMM_OK;
+  }
+  if (x == nullptr || y == nullptr) return fail(QMM_ERR_ARG, "%s: NULL x or y", fn);
+  if (!aligned16(x) || !aligned16(y))
+    return fail(QMM_ERR_ARG, "%s: x and y must be 16-byte aligned", fn);
+  return QMM_OK;
+}
+
+qmm_status check_workspace(const char* fn, size_t need, const void* ws, size_t ws_bytes) {
+  if (need == 0) return QMM_OK;
+  if (ws == nullptr || ws_bytes < need)
+    return fail(QMM_ERR_ARG, "%s: workspace of %zu bytes needed (got %zu%s)", fn, need, ws_bytes,
+                ws ? "" : ", NULL");
+  if (!aligned16(ws)) return fail(QMM_ERR_ARG, "%s: workspace must be 16-byte aligned", fn);
+  return QMM_OK;
+}
+
+qmm_status device_status(const char* fn, hipError_t e) {
+  if (e != hipSuccess)
+    return fail(QMM_ERR_DEVICE, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+  return ok();
+}
+
+bool gemv_shape_ok(int N, int K, int w_bit) {
+  return w_bit == 8 ? (K % 16 == 0) : (N % 4 == 0);
+}
+
+bool gemm_shape_ok(int N, int K, int w_bit) {
+  return N % 16 == 0 && K % qmm::mfma_kblock(w_bit) == 0;
+}
+
+}  // namespace
+
+namespace qmm {
+int env_int(const char* name) {
+  const char* v = getenv(name);
+  if (v == nullptr || *v == '\0') return -1;
+  return atoi(v);
+}
+}  // namespace qmm
+
+extern "C" {
+
+int qmm_version(void) { return (0 << 16) | 1; }
+
+const char* qmm_last_error(void) { return g_err; }
+
+size_t qmm_packed_bytes(int N, int K, int w_bit, int layout) {
+  if (N < 0 || K < 0) return 0;
+  if (w_bit != 2 && w_bit != 4 && w_bit != 8) return 0;
+  if (layout == QMM_LAYOUT_CANON) {
+    if (w_bit != 8 && K % (32 / w_bit) != 0) return 0;
+  } else if (layout == QMM_LAYOUT_MFMA) {
+    if (!gemm_shape_ok(N, K, w_bit)) return 0;
+  } else {
+    return 0;
+  }
+  return (size_t)N * K * w_bit / 8;
+}
+
+static qmm_status layout_call(const char* fn, const void* src, void* dst, int N, int K,
+                              int w_bit, void* stream, bool to_mfma) {
+  if (N < 0 || K < 0) return fail(QMM_ERR_ARG, "%s: negative size N=%d K=%d", fn, N, K);
+  if (w_bit != 2 && w_bit != 4 && w_bit != 8)
+    return fail(QMM_ERR_ARG, "%s: w_bit must be 2, 4 or 8 (got %d)", fn, w_bit);
+  if (N == 0 || K == 0) return ok();
+  if (!gemm_shape_ok(N, K, w_bit))
+    return fail(QMM_ERR_UNSUPPORTED, "%s: tile layout needs N %% 16 == 0 and K %% %d == 0", fn,
+                qmm::mfma_kblock(w_bit));
+  if (src == nullptr || dst == nullptr) return fail(QMM_ERR_ARG, "%s: NULL buffer", fn);
+  if (!aligned16(src) || !aligned16(dst))
+    return fail(QMM_ERR_ARG, "%s: buffers must be 16-byte aligned", fn);
+  const size_t bytes = (size_t)N * K * w_bit / 8;
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  if (a < b + bytes && b < a + bytes) return fail(QMM_ERR_ARG, "%s: buffers overlap", fn);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = to_mfma ? qmm::launch_pack(src, dst, N, K, w_bit, s)
+                         : qmm::launch_unpack_layout(src, dst, N, K, w_bit, s);
+  return device_status(fn, e);
+}
+
+qmm_status qmm_pack(const void* Q_canon, void* Q_mfma, int N, int K, int w_bit, void* stream) {
+  return layout_call("qmm_pack", Q_canon, Q_mfma, N, K, w_bit, stream, true);
+}
+
+qmm_status qmm_unpack_layout(const void* Q_mfma, void* Q_canon, int N, int K, int w_bit,
+                             void* stream) {
+  return layout_call("qmm_unpack_layout", Q_mfma, Q_canon, N, K, w_bit, stream, false);
+}
+
+size_t qmm_workspace_bytes(int M, int N, int K, int w_bit, int group_size) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  if (w_bit != 2 && w_bit != 4 && w_bit != 8) return 0;
+  if (w_bit != 8 && (group_size <= 0 || K % group_size != 0 || !group_supported(group_size)))
+    return 0;
+  size_t need = 0;
+  if (M <= 16 && w_bit != 8 && gemv_shape_ok(N, K, w_bit)) {
+    const size_t g = qmm::plan_gemv_lowbit(M, N, K, w_bit, group_size).workspace_bytes;
+    if (g > need) need = g;
+  }
+  if (gemm_shape_ok(N, K, w_bit)) {
+    const size_t g = qmm::plan_gemm(M, N, K, w_bit, group_size).workspace_bytes;
+    if (g > need) need = g;
+  }
+  return need;
+}
+
+qmm_status qmm_gemv(const void* x, const void* Q, const void* scales, const void* zeros, float* y,
+                    int M, int N, int K, int w_bit, int group_size, int x_dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  const char* fn = "qmm_gemv";
+  bool noop = false;
+  qmm_status st = check_matmul(fn, x, Q, scales, zeros, y, M, N, K, w_bit, group_size, x_dtype,
+                               &noop);
+  if (st != QMM_OK) return st;
+  if (noop) return ok();
+  if (M > 16)
+    return fail(QMM_ERR_UNSUPPORTED, "%s: M=%d > 16; use qmm_gemm for larger batches", fn, M);
+  if (!gemv_shape_ok(N, K, w_bit))
+    return fail(QMM_ERR_UNSUPPORTED, "%s: needs %s", fn,
+                w_bit == 8 ? "K % 16 == 0 for int8" : "N % 4 == 0 for low-bit weights");
+  qmm::MatmulArgs a{x, Q, scales, zeros, y, M, N, K, w_bit, group_size, x_dtype, workspace,
+                    reinterpret_cast<hipStream_t>(stream)};
+  if (w_bit == 8) {
+    const qmm::GemvInt8Plan p = qmm::plan_gemv_int8(M, N, K);
+    return device_status(fn, qmm::launch_gemv_int8(a, p));
+  }
+  const qmm::GemvLowbitPlan p = qmm::plan_gemv_lowbit(M, N, K, w_bit, group_size);
+  st = check_workspace(fn, p.workspace_bytes, workspace, workspace_bytes);
+  if (st != QMM_OK) return st;
+  return device_status(fn, qmm::launch_gemv_lowbit(a, p));
+}
+
+qmm_status qmm_gemm(const void* x, const void* Q, const void* scales, const void* zeros, float* y,
+                    int M, int N, int K, int w_bit, int group_size, int x_dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  const char* fn = "qmm_gemm";
+  bool noop = false;
+  qmm_status st = check_matmul(fn, x, Q, scales, zeros, y, M, N, K, w_bit, group_size, x_dtype,
+                               &noop);
+  if (st != QMM_OK) return st;
+  if (noop) return ok();
+  if (!gemm_shape_ok(N, K, w_bit))
+    return fail(QMM_ERR_UNSUPPORTED, "%s: tile layout needs N %% 16 == 0 and K %% %d == 0", fn,
+                qmm::mfma_kblock(w_bit));
+  const qmm::GemmPlan p = qmm::plan_gemm(M, N, K, w_bit, group_size);
+  if (p.kind < 0) return fail(QMM_ERR_UNSUPPORTED, "%s: no MFMA kernel for this shape", fn);
+  st = check_workspace(fn, p.workspace_bytes, workspace, workspace_bytes);
+  if (st != QMM_OK) return st;
+  qmm::MatmulArgs a{x, Q, scales, zeros, y, M, N, K, w_bit, group_size, x_dtype, workspace,
+                    reinterpret_cast<hipStream_t>(stream)};
+  return device_status(fn, qmm::launch_gemm(a, p));
+}
+
+qmm_status qmm_dequant(const void* Q, int layout, const void* scales, const void* zeros,
+                       float* w_out, int N, int K, int w_bit, int group_size, void* stream) {
+  const char* fn = "qmm_dequant";
+  if (layout != QMM_LAYOUT_CANON && layout != QMM_LAYOUT_MFMA)
+    return fail(QMM_ERR_ARG, "%s: unknown layout %d", fn, layout);
+  bool noop = false;
+  qmm_status st = check_operands(fn, Q, scales, zeros, N, K, w_bit, group_size, &noop);
+  if (st != QMM_OK) return st;
+  if (noop) return ok();
+  if (w_out == nullptr) return fail(QMM_ERR_ARG, "%s: NULL w_out", fn);
+  if (layout == QMM_LAYOUT_MFMA && !gemm_shape_ok(N, K, w_bit))
+    return fail(QMM_ERR_UNSUPPORTED, "%s: tile layout needs N %% 16 == 0 and K %% %d == 0", fn,
+                qmm::mfma_kblock(w_bit));
+  if (layout == QMM_LAYOUT_CANON && w_bit != 8 && K % (32 / w_bit) != 0)
+    return fail(QMM_ERR_ARG, "%s: K must be a multiple of %d", fn, 32 / w_bit);
+  return device_status(fn, qmm::launch_dequant(Q, layout, scales, zeros, w_out, N, K, w_bit,
+                                               group_size,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

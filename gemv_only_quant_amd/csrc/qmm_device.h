@@ -1,0 +1,85 @@
+// qmm_device.h -- device helpers shared by the qmm HIP kernels (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+enum { XF16 = 0, XBF16 = 1 };
+
+// "Magic" exponent bias: OR-ing a small unsigned integer c into the low
+// mantissa bits of these 16-bit patterns gives the float B + c exactly
+// (fp16: 0x6400 = 1024, unit step for c < 1024; bf16: 0x4300 = 128, unit
+// step for c < 128).  The same exponent-bias idea appears in Marlin's int4
+// dequant() for fp16.
+template <int XDT> struct Bias;
+template <> struct Bias<XF16> {
+  static constexpr uint32_t pair = 0x64006400u;  // (1024, 1024)
+  static constexpr float value = 1024.0f;
+  static constexpr uint32_t one_pair = 0x3C003C00u;  // (1.0, 1.0)
+};
+template <> struct Bias<XBF16> {
+  static constexpr uint32_t pair = 0x43004300u;  // (128, 128)
+  static constexpr float value = 128.0f;
+  static constexpr uint32_t one_pair = 0x3F803F80u;
+};
+
+// acc + a.lo * b.lo + a.hi * b.hi with fp32 accumulation (v_dot2c_f32_*).
+template <int XDT> __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc);
+template <> __device__ __forceinline__ float dot2<XF16>(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b),
+                                acc, false);
+}
+template <> __device__ __forceinline__ float dot2<XBF16>(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// Two 16-bit lanes: low halves of (a, b) and high halves of (a, b).
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// One DPP-moved copy of v added to v; CTRL / ROW_MASK are DPP controls.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                 0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Full-wave sum with DPP: butterfly inside each row of 16 lanes, then the
+// row_bcast steps fold the four rows into lane 63, which is read back.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add<0x124, 0xF>(v);  // row_ror:4
+  v = dpp_add<0x128, 0xF>(v);  // row_ror:8
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Work-item remap so that consecutive work ids land on one XCD: the
+// dispatcher deals workgroups round-robin over the 8 XCDs, so block b runs
+// on XCD b % 8.  Used only when the grid is a multiple of 8.
+__device__ __forceinline__ int xcd_remap(int b, int total) {
+  if (total % 8 != 0) return b;
+  return (b % 8) * (total / 8) + b / 8;
+}
+
+}  // namespace qmm

@@ -1,0 +1,66 @@
+// qmm_internal.h -- host-side launch plans and kernel launchers (not public).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmm {
+
+// Arguments shared by every matmul launcher, already validated.
+struct MatmulArgs {
+  const void* x;
+  const void* Q;
+  const void* scales;
+  const void* zeros;
+  float* y;
+  int M, N, K, w_bit, group_size, x_dtype;
+  void* workspace;
+  hipStream_t stream;
+};
+
+// ---- low-bit GEMV on the canonical layout -------------------------------
+struct GemvLowbitPlan {
+  int mb;        // M bucket (compiled row count >= M)
+  int rl;        // packed rows per lane (divides group_size / pack)
+  int waves;     // waves per workgroup
+  int n_tiles;   // 64-column tiles
+  int ksplit;    // workgroups along K per tile
+  size_t workspace_bytes;
+};
+GemvLowbitPlan plan_gemv_lowbit(int M, int N, int K, int w_bit, int group_size);
+hipError_t launch_gemv_lowbit(const MatmulArgs& a, const GemvLowbitPlan& p);
+
+// ---- int8 GEMV on (N, K) int8 ------------------------------------------
+struct GemvInt8Plan {
+  int mb;        // M bucket
+  int rn;        // output rows (n) per wave
+  int blocks;
+};
+GemvInt8Plan plan_gemv_int8(int M, int N, int K);
+hipError_t launch_gemv_int8(const MatmulArgs& a, const GemvInt8Plan& p);
+
+// ---- repack / dequant ----------------------------------------------------
+int mfma_kblock(int w_bit);  // K extent of one 1 KiB layout block
+hipError_t launch_pack(const void* q_canon, void* q_mfma, int N, int K, int w_bit,
+                       hipStream_t s);
+hipError_t launch_unpack_layout(const void* q_mfma, void* q_canon, int N, int K, int w_bit,
+                                hipStream_t s);
+hipError_t launch_dequant(const void* Q, int layout, const void* scales, const void* zeros,
+                          float* w, int N, int K, int w_bit, int group_size, hipStream_t s);
+
+// ---- MFMA GEMM on the tile layout ---------------------------------------
+struct GemmPlan {
+  int kind;      // 0: skinny (registers-direct), 1: LDS-tiled
+  int mtile;     // rows per M tile
+  int ksplit;
+  int n_tiles;
+  int m_tiles;
+  size_t workspace_bytes;
+};
+GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size);
+hipError_t launch_gemm(const MatmulArgs& a, const GemmPlan& p);
+
+// Optional integer override from the environment (tile sweeps); -1 if unset.
+int env_int(const char* name);
+
+}  // namespace qmm

@@ -1,0 +1,148 @@
+/*
+ * qmm.h -- weight-only quantized matmul for AMD Instinct MI355X (gfx950).
+ *
+ *     y[m][n] = sum_k x[m][k] * W[k][n],     W = dequant(Q)
+ *
+ * x is fp16 or bf16, Q holds int4 / int2 codes with per-group fp16 scales
+ * and integer zero points, or int8 codes with a per-output-row fp32 scale;
+ * accumulation is fp32 and y is fp32.
+ *
+ * Where the operation is defined:
+ *  - operands and the canonical packed layout: BitDistiller,
+ *    quantization/triton_kernels.py, quant_matmul_kernel (docstring shapes
+ *    a (M,K), qw (K/pack_num, N), scales (K/group_size, N),
+ *    qzeros (K/group_size/pack_num, N); unpack "(qw >> (k % pack_num) *
+ *    w_bit) & offset"; group index floor(k / group_size));
+ *  - the symmetric int4 zero point 8: aphrodite-engine marlin_cuda_kernel.cu,
+ *    dequant() ("-8 symmetric zero point");
+ *  - int8 weights (N, K) with the fp32 row scale applied after an fp32 sum:
+ *    tiny-llm src/tinyllm/kernels/int8_gemv.py (module and int8_matmul
+ *    docstrings);
+ *  - the zero-size early return: marlin_cuda_kernel.cu, marlin_cuda().
+ *
+ * Conventions for every entry point
+ *  - Data pointers are DEVICE pointers owned by the caller, contiguous,
+ *    row-major and 16-byte aligned.  `stream` is a hipStream_t passed as
+ *    void* (NULL = the null stream).  Calls are asynchronous on `stream`,
+ *    never synchronise and never allocate.
+ *  - Every argument is checked before any HIP call; a failing call returns a
+ *    status, launches nothing and sets a thread-local message read with
+ *    qmm_last_error().
+ *  - M == 0, N == 0 or K == 0 (with otherwise valid arguments) is a no-op
+ *    returning QMM_OK.
+ *
+ * Operand table (pack = 32 / w_bit, G = K / group_size, Zr = ceil(G / pack))
+ *   w_bit 4 or 2:
+ *     Q       canonical: (K/pack, N) int32; code k of column n at bit
+ *             (k % pack) * w_bit of word [k / pack][n], low field first.
+ *             MFMA layout: see qmm_pack.
+ *     scales  (G, N) fp16
+ *     zeros   NULL (symmetric, z = 2^(w_bit-1): 8 for int4, 2 for int2) or
+ *             (Zr, N) int32, zero of group g at bit (g % pack) * w_bit of
+ *             word [g / pack][n] (fields past G are ignored)
+ *     group_size in {32, 64, 128, 256}, K % group_size == 0
+ *     W[k][n] = (q - z) * s[k / group_size][n]
+ *   w_bit 8:
+ *     Q       (N, K) int8 (two's complement), same in both layouts' inputs
+ *     scales  (N,) fp32; zeros must be NULL; group_size must be 0
+ *     y[m][n] = scales[n] * sum_k x[m][k] * Q[n][k]
+ *   x (M, K) fp16 or bf16 (x_dtype), y (M, N) fp32, fully overwritten.
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define QMM_API __attribute__((visibility("default")))
+#else
+#define QMM_API
+#endif
+
+typedef enum {
+    QMM_OK = 0,
+    QMM_ERR_ARG = 1,          /* invalid argument (NULL, negative, bad enum, misaligned,
+                                 K % group_size, workspace too small, ...) */
+    QMM_ERR_UNSUPPORTED = 2,  /* valid but not built: shape or group size outside
+                                 the supported set, M > 16 on qmm_gemv */
+    QMM_ERR_DEVICE = 3        /* a HIP call or kernel launch failed */
+} qmm_status;
+
+typedef enum { QMM_F16 = 0, QMM_BF16 = 1 } qmm_dtype;
+typedef enum { QMM_LAYOUT_CANON = 0, QMM_LAYOUT_MFMA = 1 } qmm_layout;
+
+/* Library version, (major << 16) | minor. */
+QMM_API int qmm_version(void);
+
+/* Message describing the last failing call on this thread ("" if none). */
+QMM_API const char* qmm_last_error(void);
+
+/* Bytes of Q for an (N, K) weight in `layout`; 0 if the combination is
+ * invalid.  Both layouts hold N*K*w_bit/8 bytes. */
+QMM_API size_t qmm_packed_bytes(int N, int K, int w_bit, int layout);
+
+/*
+ * qmm_pack: canonical Q -> MFMA tile layout (offline, integer bijection).
+ * The pages print no repack routine (Marlin consumes a pre-permuted B but
+ * its permutation is not shown), so this layout is this library's own:
+ *   columns in strips of 16, K in blocks of KB = 128 (int4), 256 (int2)
+ *   or 64 (int8); block (strip s, K-block kb) is 1024 contiguous bytes at
+ *   offset 1024 * (s * (K/KB) + kb).  Bytes [16 L, 16 L + 16) of a block
+ *   ("lane" L in 0..63) serve column 16 s + L % 16 and k-octet c = L / 16:
+ *     int4: int32 word j (0..3) holds k = 128 kb + 32 j + 8 c + i (i 0..7),
+ *           code i in nibble i/2 for even i, 4 + i/2 for odd i;
+ *     int2: word j holds k = 256 kb + 64 j + 32 h + 8 c + i (h 0..1),
+ *           code in 2-bit field 4 h + i/2 (even i) or 8 + 4 h + i/2 (odd i);
+ *     int8: byte 8 h + i holds k = 64 kb + 32 h + 8 c + i.
+ * Requires N % 16 == 0 and K % KB == 0.  Q_canon and Q_mfma must not
+ * overlap.  qmm_unpack_layout is the exact inverse.
+ */
+QMM_API qmm_status qmm_pack(const void* Q_canon, void* Q_mfma, int N, int K, int w_bit, void* stream);
+QMM_API qmm_status qmm_unpack_layout(const void* Q_mfma, void* Q_canon, int N, int K, int w_bit,
+                             void* stream);
+
+/*
+ * Workspace for qmm_gemv / qmm_gemm (split-K partial sums and arrival
+ * counters).  Caller-owned device memory of at least
+ * qmm_workspace_bytes(...) bytes, ZERO-FILLED ONCE when allocated; every
+ * call leaves its counters at zero again, so one workspace serves any
+ * number of successive calls on one stream.  Calls that may run
+ * concurrently need distinct workspaces.  The size covers both entry
+ * points for the given shape; it may be 0 (workspace may then be NULL).
+ */
+QMM_API size_t qmm_workspace_bytes(int M, int N, int K, int w_bit, int group_size);
+
+/*
+ * qmm_gemv: decode / skinny path, 1 <= M <= 16, Q in the CANONICAL layout.
+ * Streams each packed weight byte once per call.  Low-bit: N % 4 == 0.
+ * int8: K % 16 == 0.  M > 16 returns QMM_ERR_UNSUPPORTED (cf. the int8
+ * decode kernel's MAX_M row limit in tiny-llm int8_gemv.py).
+ */
+QMM_API qmm_status qmm_gemv(const void* x, const void* Q, const void* scales, const void* zeros,
+                    float* y, int M, int N, int K, int w_bit, int group_size, int x_dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qmm_gemm: any M >= 1, Q in the MFMA layout produced by qmm_pack
+ * (N % 16 == 0, K % KB == 0).  Contraction on the matrix cores.
+ */
+QMM_API qmm_status qmm_gemm(const void* x, const void* Q, const void* scales, const void* zeros,
+                    float* y, int M, int N, int K, int w_bit, int group_size, int x_dtype,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qmm_dequant: W (K, N) fp32 from Q in either layout, bit-exact:
+ * W[k][n] = float(q - z) * float(s) for low-bit (exact in fp32), and
+ * W[k][n] = float(Q[n][k]) for int8 (row scale NOT applied).  For tests.
+ */
+QMM_API qmm_status qmm_dequant(const void* Q, int layout, const void* scales, const void* zeros,
+                       float* w_out, int N, int K, int w_bit, int group_size, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMM_H */
