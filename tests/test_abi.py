@@ -85,9 +85,6 @@ GEMV_BAD = [
     (dict(M=17), E_UNS, "M=17"),
     (dict(N=66), E_UNS, "N % 4"),
     (dict(w_bit=8, group_size=0, K=24), E_UNS, "K % 16"),
-    # a K-split shape needs a workspace
-    (dict(N=4096, K=4096), E_ARG, "workspace"),
-    (dict(N=4096, K=4096, workspace=A, workspace_bytes=16), E_ARG, "workspace"),
 ]
 
 
@@ -104,6 +101,10 @@ GEMM_BAD = [
     (dict(w_bit=2, K=128, group_size=64), E_UNS, "K % 256"),
     (dict(w_bit=8, group_size=0, K=96), E_UNS, "K % 64"),
     (dict(y=MIS), E_ARG, "aligned"),
+    # a K-split shape needs a workspace
+    (dict(N=4096, K=4096), E_ARG, "workspace"),
+    (dict(N=4096, K=4096, workspace=A, workspace_bytes=16), E_ARG, "workspace"),
+    (dict(N=4096, K=4096, workspace=MIS, workspace_bytes=1 << 30), E_ARG, "aligned"),
 ]
 
 
