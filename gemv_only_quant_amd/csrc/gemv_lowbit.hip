@@ -29,8 +29,8 @@
 
 namespace qmm {
 
-template <int W_BIT, int XDT, int MB, int RL>
-__global__ __launch_bounds__(256) void gemv_lowbit_kernel(
+template <int W_BIT, int XDT, int MB, int RL, int CQ, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemv_lowbit_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
     const uint16_t* __restrict__ sc, const uint32_t* __restrict__ qz, float* __restrict__ y,
     int M, int N, int K, int group_size) {
@@ -38,8 +38,8 @@ __global__ __launch_bounds__(256) void gemv_lowbit_kernel(
   constexpr int PAIRS = PACK / 2;    // 16-bit pairs per word
   constexpr uint32_t FIELD2 = W_BIT == 4 ? 0x000F000Fu : 0x00030003u;
   constexpr uint32_t ZMASK = (1u << W_BIT) - 1u;
-  constexpr int WAVES = 4;
-  constexpr int CQ = 4;                      // column quads per workgroup
+  constexpr int NT = 64 * WAVES;             // threads
+  constexpr int CW = 4 * CQ;                 // columns per workgroup
   constexpr int GROUPS = WAVES * 64 / CQ;    // row-lanes per workgroup
   constexpr int ROWS_P = RL * GROUPS;        // packed rows per pass
   constexpr int GSTRIDE = RL * PAIRS + 4;    // dwords per row-lane in LDS (+16 B pad)
@@ -50,12 +50,12 @@ __global__ __launch_bounds__(256) void gemv_lowbit_kernel(
   const int cq = lane % CQ;
   const int grp = wave * (64 / CQ) + lane / CQ;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int n0 = tile * 4 * CQ + cq * 4;
+  const int n0 = tile * CW + cq * 4;
   const bool col_ok = n0 < N;  // N % 4 == 0: the quad is all in or all out
 
   __shared__ uint32_t xl[MB * GROUPS * GSTRIDE];
   constexpr int ITEMS = MB * ROWS_P;
-  constexpr int PER_T = (ITEMS + 255) / 256;
+  constexpr int PER_T = (ITEMS + NT - 1) / NT;
 
   float r[MB][4];
 #pragma unroll
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void gemv_lowbit_kernel(
     u32x4_t xr[PER_T][PACK / 8];
 #pragma unroll
     for (int j = 0; j < PER_T; ++j) {
-      const int it = threadIdx.x + j * 256;
+      const int it = threadIdx.x + j * NT;
       const int m = it / ROWS_P, rr = it % ROWS_P;
       const bool ok = it < ITEMS && m < M && r_base + rr < rows;
 #pragma unroll
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void gemv_lowbit_kernel(
     if (p > 0) __syncthreads();  // previous pass done reading xl
 #pragma unroll
     for (int j = 0; j < PER_T; ++j) {
-      const int it = threadIdx.x + j * 256;
+      const int it = threadIdx.x + j * NT;
       if (it < ITEMS) {
         const int m = it / ROWS_P, rr = it % ROWS_P;
         uint32_t* dst = xl + (m * GROUPS + rr / RL) * GSTRIDE + (rr % RL) * PAIRS;
@@ -180,29 +180,27 @@ __global__ __launch_bounds__(256) void gemv_lowbit_kernel(
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       float v = r[m][c];
-      v += __shfl_xor(v, 4);
-      v += __shfl_xor(v, 8);
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
+#pragma unroll
+      for (int b = CQ; b < 64; b *= 2) v += __shfl_xor(v, b);
       r[m][c] = v;
     }
   __syncthreads();
-  float* red = reinterpret_cast<float*>(xl);  // [WAVES][MB][16]
-  static_assert(WAVES * MB * 16 <= MB * GROUPS * GSTRIDE, "LDS reuse");
+  float* red = reinterpret_cast<float*>(xl);  // [WAVES][MB][CW]
+  static_assert(WAVES * MB * CW <= MB * GROUPS * GSTRIDE, "LDS reuse");
   if (lane < CQ) {
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) red[(wave * MB + m) * 16 + cq * 4 + c] = r[m][c];
+      for (int c = 0; c < 4; ++c) red[(wave * MB + m) * CW + cq * 4 + c] = r[m][c];
   }
   __syncthreads();
-  for (int o = threadIdx.x; o < MB * 16; o += 256) {
-    const int m = o >> 4, col = o & 15;
-    const int n = tile * 16 + col;
+  for (int o = threadIdx.x; o < MB * CW; o += NT) {
+    const int m = o / CW, col = o % CW;
+    const int n = tile * CW + col;
     if (m < M && n < N) {
       float sum = 0.f;
 #pragma unroll
-      for (int v = 0; v < WAVES; ++v) sum += red[(v * MB + m) * 16 + col];
+      for (int v = 0; v < WAVES; ++v) sum += red[(v * MB + m) * CW + col];
       y[(size_t)m * N + n] = sum;
     }
   }
@@ -213,8 +211,8 @@ static int m_bucket(int M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 
 
 // LDS of one pass's x slice (64 row-lanes, +16 B pad each), kept within
 // 80 KiB so a workgroup always fits the CU.
-static constexpr size_t x_lds_bytes(int mb, int rl, int pairs) {
-  return (size_t)mb * 64 * (rl * pairs + 4) * 4;
+static constexpr size_t x_lds_bytes(int mb, int rl, int pairs, int groups = 64) {
+  return (size_t)mb * groups * (rl * pairs + 4) * 4;
 }
 static constexpr size_t kXldsMax = 80 * 1024;
 
@@ -245,7 +243,7 @@ static hipError_t launch_rl(const MatmulArgs& a, const GemvLowbitPlan& p) {
   if constexpr (x_lds_bytes(MB, RL, 16 / W_BIT) > kXldsMax && RL > 2) {
     return hipErrorInvalidValue;  // never planned
   } else {
-  hipLaunchKernelGGL((gemv_lowbit_kernel<W_BIT, XDT, MB, RL>), dim3(p.n_tiles), dim3(256), 0,
+  hipLaunchKernelGGL((gemv_lowbit_kernel<W_BIT, XDT, MB, RL, 4, 4>), dim3(p.n_tiles), dim3(256), 0,
                      a.stream, reinterpret_cast<const uint16_t*>(a.x),
                      reinterpret_cast<const uint32_t*>(a.Q),
                      reinterpret_cast<const uint16_t*>(a.scales),

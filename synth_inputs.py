@@ -127,7 +127,7 @@ def one_hot(case: Case, ks):
                 case.x_dtype, x, case.Q, case.scales, case.zeros)
 
 
-# The five synthetic workloads: name -> builder.  Seed = 1000 * config + variant.
+# The synthetic workloads: name -> builder, each with a fixed seed.
 def workload(name):
     if name == "int8_gemv_m1_k1024_n1024":
         return int8_case(1, 1024, 1024, BF16, seed=1000, name=name)
