@@ -86,95 +86,80 @@ __device__ __forceinline__ u32x4_t bfrag(const u32x4_t* slot, int st) {
   return b;
 }
 
-template <int W_BIT, int XDT, int GS, int MT, int NT>
+template <int W_BIT, int XDT, int GS, int MT, int NT, int DEPTH>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ Qt,
     const void* __restrict__ scales, const uint32_t* __restrict__ qz, float* __restrict__ y,
-    float* __restrict__ part, unsigned* __restrict__ ticket, int M, int N, int K, int ksplit,
-    int n_tiles) {
+    int M, int N, int K, int n_tiles) {
   constexpr int WAVES = 4;
   constexpr int KB = Stage<W_BIT>::KB;
   constexpr int BLK = Stage<W_BIT>::BLK;
   constexpr int KS = KB * BLK;           // k per stage
   constexpr int STEPS = KS / 32;         // MFMA k steps per stage
-  constexpr int ROWS = 16 * MT;          // x rows per workgroup
-  constexpr int XROW = KS + 8;           // LDS row stride in halves (16 B pad)
-  constexpr int CHUNKS = ROWS * KS / 8;  // 16-byte x chunks per stage
-  constexpr int XPT = (CHUNKS + 255) / 256;
   constexpr bool LOWBIT = W_BIT != 8;
   constexpr int PACK = LOWBIT ? Stage<W_BIT>::PACK : 1;
   constexpr int GSZ = LOWBIT ? GS : KS;
   constexpr int NGS = GSZ < KS ? KS / GSZ : 1;  // groups touched per stage
   constexpr float CB = OpBias<W_BIT, XDT>::value;
-
-  __shared__ uint16_t xl[2][ROWS * XROW];
-  __shared__ int last_flag;
+  constexpr uint32_t ZSYM = W_BIT == 4 ? 0x88888888u : 0xAAAAAAAAu;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int l16 = lane & 15, quad = lane >> 4;
-
   const int w = xcd_remap(blockIdx.x, gridDim.x);
-  const int ks = w % ksplit;
-  const int tile = w / ksplit;
-  const int nt = tile % n_tiles, mt_idx = tile / n_tiles;
-  const int m0 = mt_idx * ROWS;
+  const int nt = w % n_tiles, mt_idx = w / n_tiles;
+  const int m0 = mt_idx * 16 * MT;
   const int strips = N / 16;
-  const int s0 = (nt * WAVES + wave) * NT;
+  const int s0 = nt * NT;
   const int nblk = K / KB;
   const int nst = (nblk + BLK - 1) / BLK;  // stages along K
-  const int per = (nst + ksplit - 1) / ksplit;
-  const int st0 = ks * per;
+  // this wave's quarter of the stages
+  const int per = (nst + WAVES - 1) / WAVES;
+  const int st0 = min(nst, wave * per);
   const int st1 = min(nst, st0 + per);
 
-  bool sval[NT];
+  int sidx[NT];
 #pragma unroll
-  for (int s = 0; s < NT; ++s) sval[s] = s0 + s < strips;
+  for (int s = 0; s < NT; ++s) sidx[s] = min(s0 + s, strips - 1);  // loads stay in bounds
+  int xrow[MT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i) xrow[i] = min(m0 + 16 * i + l16, M - 1);
 
-  // One stage in registers: weight slots, scales and zero words of the
-  // groups it touches, and this thread's share of the x tile.
+  // One stage in registers: weight slots, x operand fragments, and the
+  // scales / zero words of the groups the stage touches.
   struct StageRegs {
     u32x4_t w[NT][BLK];
+    u32x4_t a[MT][STEPS];
     uint32_t sc[NT][NGS];
     uint32_t zw[NT];
-    u32x4_t xr[XPT];
   };
   auto load_stage = [&](int st, StageRegs& R) {
 #pragma unroll
-    for (int j = 0; j < XPT; ++j) {
-      const int c = threadIdx.x + 256 * j;
-      const int row = c / (KS / 8), col = st * KS + (c % (KS / 8)) * 8;
-      const int m = m0 + row;
-      R.xr[j] = (c < CHUNKS && m < M && col < K)
-                    ? *reinterpret_cast<const u32x4_t*>(x + (size_t)m * K + col)
-                    : u32x4_t{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int s = 0; s < NT; ++s) {
+    for (int s = 0; s < NT; ++s)
 #pragma unroll
       for (int b = 0; b < BLK; ++b) {
-        const int kb = st * BLK + b;
-        R.w[s][b] = (sval[s] && kb < nblk) ? Qt[((size_t)(s0 + s) * nblk + kb) * 64 + lane]
-                                           : u32x4_t{0u, 0u, 0u, 0u};
+        const int kb = min(st * BLK + b, nblk - 1);
+        R.w[s][b] = Qt[((size_t)sidx[s] * nblk + kb) * 64 + lane];
       }
-      if constexpr (LOWBIT) {
-        const int n = 16 * (s0 + s) + l16;
-        const int g0 = (st * KS) / GS;
-        const uint16_t* s16 = reinterpret_cast<const uint16_t*>(scales);
 #pragma unroll
-        for (int q = 0; q < NGS; ++q)
-          R.sc[s][q] = sval[s] ? s16[(size_t)(g0 + q) * N + n] : 0u;
-        R.zw[s] = (qz != nullptr && sval[s]) ? qz[(size_t)(g0 / PACK) * N + n] : 0u;
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int k = 0; k < STEPS; ++k) {
+        // int8 stages are two 64-deep blocks: past the last block (odd block
+        // count) x is zero, so that half adds nothing
+        const int col = st * KS + 32 * k + 8 * quad;
+        R.a[i][k] = col < K ? *reinterpret_cast<const u32x4_t*>(x + (size_t)xrow[i] * K + col)
+                            : u32x4_t{0u, 0u, 0u, 0u};
       }
-    }
-  };
-  auto store_x = [&](const StageRegs& R, int buf) {
+    if constexpr (LOWBIT) {
+      const int g0 = (st * KS) / GS;
+      const uint16_t* s16 = reinterpret_cast<const uint16_t*>(scales);
 #pragma unroll
-    for (int j = 0; j < XPT; ++j) {
-      const int c = threadIdx.x + 256 * j;
-      if (c < CHUNKS) {
-        const int row = c / (KS / 8), col = (c % (KS / 8)) * 8;
-        *reinterpret_cast<u32x4_t*>(&xl[buf][row * XROW + col]) = R.xr[j];
+      for (int s = 0; s < NT; ++s) {
+        const int n = 16 * sidx[s] + l16;
+#pragma unroll
+        for (int q = 0; q < NGS; ++q) R.sc[s][q] = s16[(size_t)(g0 + q) * N + n];
+        R.zw[s] = qz != nullptr ? qz[(size_t)(g0 / PACK) * N + n] : ZSYM;
       }
     }
   };
@@ -203,167 +188,484 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
       xs[i] = zero4;
     }
   };
-  // scale and (bias + zero) of group q of the current stage
-  auto group_consts = [&](const StageRegs& R, int st, int q, float (&sc)[NT], float (&bz)[NT]) {
-    const int g = (st * KS) / GS + q;
+
+  auto compute_stage = [&](int st, const StageRegs& R, bool last) {
 #pragma unroll
-    for (int s = 0; s < NT; ++s) {
-      sc[s] = f16_bits_to_f32((uint16_t)R.sc[s][q]);
-      const uint32_t z = qz != nullptr ? (R.zw[s] >> ((g % PACK) * W_BIT)) & ((1u << W_BIT) - 1u)
-                                       : (1u << (W_BIT - 1));
-      bz[s] = CB + (float)z;
+    for (int k = 0; k < STEPS; ++k) {
+#pragma unroll
+      for (int i = 0; i < MT; ++i) xs[i] = mfma16<XDT>(R.a[i][k], ones, xs[i]);
+#pragma unroll
+      for (int s = 0; s < NT; ++s) {
+        const u32x4_t b = bfrag<W_BIT, XDT>(R.w[s], k);
+#pragma unroll
+        for (int i = 0; i < MT; ++i) acc[i][s] = mfma16<XDT>(R.a[i][k], b, acc[i][s]);
+      }
+      if constexpr (LOWBIT) {
+        const int kend = st * KS + 32 * (k + 1);  // one past this step
+        if (kend % GS == 0 || (k == STEPS - 1 && last)) {
+          const int q = GS < KS ? (32 * k) / GS : 0;
+          const int g = (st * KS) / GS + q;
+          float sc[NT], bz[NT];
+#pragma unroll
+          for (int s = 0; s < NT; ++s) {
+            sc[s] = f16_bits_to_f32((uint16_t)R.sc[s][q]);
+            bz[s] = CB + (float)((R.zw[s] >> ((g % PACK) * W_BIT)) & ((1u << W_BIT) - 1u));
+          }
+          flush(sc, bz);
+        }
+      }
     }
   };
 
+  // DEPTH-deep ring of stages in registers: stage st + DEPTH is requested
+  // while stage st computes (loads past the range re-read its last stage)
   if (st0 < st1) {
-    StageRegs cur, nxt;
-    load_stage(st0, cur);
-    store_x(cur, 0);
-    __syncthreads();
-    for (int st = st0; st < st1; ++st) {
-      const int buf = (st - st0) & 1;
-      const bool more = st + 1 < st1;
-      if (more) load_stage(st + 1, nxt);
-      const uint16_t* xb = xl[buf];
+    StageRegs ring[DEPTH];
 #pragma unroll
-      for (int k = 0; k < STEPS; ++k) {
-        u32x4_t a[MT];
+    for (int d = 0; d < DEPTH; ++d) load_stage(min(st0 + d, st1 - 1), ring[d]);
+    for (int st = st0; st < st1; st += DEPTH) {
 #pragma unroll
-        for (int i = 0; i < MT; ++i) {
-          a[i] = *reinterpret_cast<const u32x4_t*>(&xb[(16 * i + l16) * XROW + 32 * k + 8 * quad]);
-          xs[i] = mfma16<XDT>(a[i], ones, xs[i]);
-        }
-#pragma unroll
-        for (int s = 0; s < NT; ++s) {
-          const u32x4_t b = bfrag<W_BIT, XDT>(cur.w[s], k);
-#pragma unroll
-          for (int i = 0; i < MT; ++i) acc[i][s] = mfma16<XDT>(a[i], b, acc[i][s]);
-        }
-        if constexpr (LOWBIT) {
-          const int kend = st * KS + 32 * (k + 1);  // one past this step
-          if (kend % GS == 0 || (k == STEPS - 1 && !more)) {
-            float sc[NT], bz[NT];
-            group_consts(cur, st, GS < KS ? (32 * k) / GS : 0, sc, bz);
-            flush(sc, bz);
-          }
+      for (int d = 0; d < DEPTH; ++d) {
+        if (st + d < st1) {
+          compute_stage(st + d, ring[d], st + d == st1 - 1);
+          load_stage(min(st + d + DEPTH, st1 - 1), ring[d]);
         }
       }
-      if (more) {
-        store_x(nxt, buf ^ 1);
-        cur = nxt;
-      }
-      __syncthreads();
     }
   }
   if constexpr (!LOWBIT) {
     float sc[NT], bz[NT];
 #pragma unroll
     for (int s = 0; s < NT; ++s) {
-      sc[s] = sval[s] ? reinterpret_cast<const float*>(scales)[16 * (s0 + s) + l16] : 0.f;
+      sc[s] = reinterpret_cast<const float*>(scales)[16 * sidx[s] + l16];
       bz[s] = CB;
     }
     flush(sc, bz);
   }
 
-  // ---- write the tile (or this K-range's partial) ----------------------
+  // ---- the 4 K-quarters meet in LDS ------------------------------------
+  constexpr int ROWS = 16 * MT, COLS = 16 * NT;
+  __shared__ float red[WAVES][ROWS][COLS + 1];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
-    for (int s = 0; s < NT; ++s) {
-      if (!sval[s]) continue;
-      const int n = 16 * (s0 + s) + l16;
+    for (int s = 0; s < NT; ++s)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 16 * i + 4 * quad + r;
-        if (m < M) {
-          if (ksplit == 1) y[(size_t)m * N + n] = yacc[i][s][r];
-          else part[((size_t)ks * M + m) * N + n] = yacc[i][s][r];
-        }
-      }
-    }
-  if (ksplit == 1) return;
-
-  __threadfence();
+      for (int r = 0; r < 4; ++r) red[wave][16 * i + 4 * quad + r][16 * s + l16] = yacc[i][s][r];
   __syncthreads();
-  if (threadIdx.x == 0) last_flag = (atomicAdd(&ticket[tile], 1u) == (unsigned)(ksplit - 1));
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  const int ncols = 16 * NT * WAVES;
-  const int n_first = 16 * nt * NT * WAVES;
-  for (int o = threadIdx.x; o < ROWS * ncols; o += 256) {
-    const int m = m0 + o / ncols, n = n_first + o % ncols;
+  for (int o = threadIdx.x; o < ROWS * COLS; o += 256) {
+    const int rr = o / COLS, cc = o % COLS;
+    const int m = m0 + rr, n = 16 * s0 + cc;
     if (m < M && n < N) {
       float sum = 0.f;
-      for (int j = 0; j < ksplit; ++j) sum += part[((size_t)j * M + m) * N + n];
+#pragma unroll
+      for (int v = 0; v < WAVES; ++v) sum += red[v][rr][cc];
       y[(size_t)m * N + n] = sum;
     }
   }
-  if (threadIdx.x == 0) atomicExch(&ticket[tile], 0u);
+}
+
+// ---------------------------------------------------------------------------
+// Large-M kernel (prefill), matrix-core bound.
+//  * workgroup tile 256 x 256, 4 waves side by side along N: a wave owns all
+//    256 rows x 4 strips (64 columns) = 16 x 4 MFMA tiles, 256 fp32
+//    accumulators per lane (the matrix-core register file);
+//  * weights: each wave streams its own 4 strips straight from the tile
+//    layout into B operands (no LDS, no duplication across waves) and
+//    dequantizes them to the MFMA's 16-bit type: w = (q - z) * s is formed
+//    exactly in fp32 (a 4-bit by 11-bit product) and rounded once to
+//    fp16 / bf16 (round to nearest even);
+//  * x: the 256 x 128 tile of a stage is shared by the 4 waves through
+//    double-buffered LDS, stored fragment-major (16 rows x 32 k = one 1 KiB
+//    block in MFMA A-operand lane order), so every operand read is one
+//    conflict-free ds_read_b128;
+//  * stage s + 1's x tile and weight slots are loaded while stage s runs.
+template <int XDT> struct WType;
+template <> struct WType<XF16> {
+  // (a, b) fp32 -> packed fp16 pair, round to nearest even
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    half2_t h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+};
+template <> struct WType<XBF16> {
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    bf16x2_t h = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+};
+
+// B operand (8 dequantized weights of one column) for k step `st` of a
+// 128-deep stage: int4 word st of the slot; int2 word st / 2, k half st % 2.
+// sc = scale, zs = z * scale of the step's group: w = q * s - z * s, exact.
+template <int W_BIT, int XDT>
+__device__ __forceinline__ u32x4_t bfrag_scaled(const u32x4_t& slot, int st, float sc, float zs) {
+  float f[8];
+  if constexpr (W_BIT == 4) {
+    const uint32_t w = slot[st];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int field = (i & 1) ? 4 + (i >> 1) : (i >> 1);
+      f[i] = (float)((w >> (4 * field)) & 0xFu);
+    }
+  } else {
+    const uint32_t w = slot[st >> 1];
+    const int h = st & 1;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int field = (i & 1) ? 8 + 4 * h + (i >> 1) : 4 * h + (i >> 1);
+      f[i] = (float)((w >> (2 * field)) & 0x3u);
+    }
+  }
+  u32x4_t b;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    b[t] = WType<XDT>::pack(__builtin_fmaf(f[2 * t], sc, -zs), __builtin_fmaf(f[2 * t + 1], sc, -zs));
+  return b;
+}
+
+// MFMA whose accumulator is pinned to the matrix-core (AGPR) registers: the
+// large-M kernel keeps 256 accumulators per lane live across its K loop,
+// and without the pin the register allocator shuttles them between register
+// files every iteration.  Independent MFMAs sit between two uses of the same
+// accumulator, so no extra wait states are needed inside the loop.
+template <int XDT> __device__ __forceinline__ void mfma16_acc(f32x4_t& c, const u32x4_t& a,
+                                                             const u32x4_t& b);
+template <> __device__ __forceinline__ void mfma16_acc<XF16>(f32x4_t& c, const u32x4_t& a,
+                                                            const u32x4_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+template <> __device__ __forceinline__ void mfma16_acc<XBF16>(f32x4_t& c, const u32x4_t& a,
+                                                             const u32x4_t& b) {
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// 16-row tiles per wave in the large-M kernel (rows per workgroup / 16):
+// 16 (one wave per SIMD, 256 accumulators) or 8 (two waves per SIMD).
+static int large_mt() {
+  const int e = env_int("QMM_LARGE_MT");
+  return (e == 8 || e == 16) ? e : 16;
+}
+
+// s_waitcnt with vmcnt = 0 and the other counters at their maximum.
+static constexpr int kWaitVm0 = 0x0F70;
+
+// Operand register t (k = 2t, 2t + 1 of one column) of a pre-scaled B
+// fragment: W = (q - z) * s rounded once to the MFMA's 16-bit type.
+// The two codes are masked into the mantissa of fp16 1024 (exact: 1024 + q),
+// then
+//   bf16: v_fma_mix_f32 forms (1024 + q) * s - (1024 + z) * s in fp32 --
+//         both products fit 22 bits and their difference (q - z) * s is
+//         representable, so the fused result is exact -- and
+//         v_cvt_pk_bf16_f32 rounds the pair to nearest even;
+//   fp16: v_pk_add_f16 gives q - z exactly, v_pk_mul_f16 rounds (q - z) * s
+//         once to nearest even.
+// int4: word bits (4t, 16 + 4t) hold fields (t, 4 + t); int2: word bits
+// (2(4h + t), 16 + 2(4h + t)) hold fields (4h + t, 8 + 4h + t).
+struct GroupConst {
+  float s;          // scale
+  float zb_s;       // (1024 + z) * s
+  uint32_t s_h2;    // scale as an fp16 pair
+  uint32_t nzb_h2;  // -(1024 + z) as an fp16 pair
+};
+
+template <int W_BIT, int XDT>
+__device__ __forceinline__ uint32_t bpair_scaled(uint32_t w, int h, int t, const GroupConst& g) {
+  constexpr uint32_t FIELD2 = W_BIT == 4 ? 0x000F000Fu : 0x00030003u;
+  const int sh = W_BIT == 4 ? 4 * t : 2 * (4 * h + t);
+  const uint32_t m = ((w >> sh) & FIELD2) | 0x64006400u;
+  const half2_t mh = __builtin_bit_cast(half2_t, m);
+  if constexpr (XDT == XBF16) {
+    const float lo = __builtin_fmaf((float)mh[0], g.s, -g.zb_s);
+    const float hi = __builtin_fmaf((float)mh[1], g.s, -g.zb_s);
+    bf16x2_t r = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, r);
+  } else {
+    const half2_t d = mh + __builtin_bit_cast(half2_t, g.nzb_h2);
+    return __builtin_bit_cast(uint32_t, d * __builtin_bit_cast(half2_t, g.s_h2));
+  }
+}
+
+template <int W_BIT, int XDT, int GS, bool ZP, int MT>
+__global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
+    const uint16_t* __restrict__ x, const u32x4_t* __restrict__ Qt,
+    const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qz, float* __restrict__ y,
+    int M, int N, int K, int n_tiles) {
+  constexpr int BM = 16 * MT;          // rows per workgroup (MT 16-row tiles)
+  constexpr int NT = 4;                 // strips per wave
+  constexpr int KS = 128;               // k per stage
+  constexpr int STEPS = KS / 32;        // MFMA k steps per stage
+  constexpr int KB = W_BIT == 4 ? 128 : 256;  // layout block depth
+  constexpr int FRAGS = MT * STEPS;     // 1 KiB A fragments per stage
+  constexpr int PACK = 32 / W_BIT;
+  constexpr int NGS = GS < KS ? KS / GS : 1;  // groups per stage
+  // symmetric zero 2^(w_bit-1) in every field of a word
+  constexpr uint32_t ZSYM = W_BIT == 4 ? 0x88888888u : 0xAAAAAAAAu;
+
+  __shared__ u32x4_t xa[2][FRAGS * 64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l16 = lane & 15, quad = lane >> 4;
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int nt = w % n_tiles, mt_idx = w / n_tiles;
+  const int m0 = mt_idx * BM;
+  const int strips = N / 16;
+  const int s0 = (nt * 4 + wave) * NT;
+  const int nblk = K / KB;
+  const int nst = K / KS;
+
+  // Loads always use a valid strip (the last one stands in for strips past
+  // N); their results are simply not stored.
+  int sidx[NT];
+#pragma unroll
+  for (int s = 0; s < NT; ++s) sidx[s] = min(s0 + s, strips - 1);
+
+  // x fragment f of a stage (row tile f / STEPS, k step f % STEPS) is one
+  // 1 KiB block in A-operand lane order: lane p holds row 16 (f / STEPS) +
+  // p % 16, k 32 (f % STEPS) + 8 (p / 16) .. + 7.  Each wave moves its
+  // FRAGS / 4 fragments straight from global memory into LDS (lane p's 16
+  // bytes land at block + 16 p).  Rows past M read row M - 1 instead: they
+  // only feed output rows that are never stored.
+  const int rows_left = M - 1 - m0;
+#if QMM_X_VIA_REGS
+  // x chunk c = threadIdx + 256 j of a stage is fragment c / 64, lane c % 64:
+  // loaded into registers at the start of a stage, written to LDS at its end
+  constexpr int XPT = FRAGS * 64 / 256;
+  u32x4_t xr[XPT];
+  auto load_x_regs = [&](int st) {
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+      const int c = threadIdx.x + 256 * j;
+      const int f = c >> 6, p = c & 63;
+      const int rr = min(16 * (f / STEPS) + (p & 15), rows_left);
+      const int k = st * KS + 32 * (f % STEPS) + 8 * (p >> 4);
+      xr[j] = *reinterpret_cast<const u32x4_t*>(x + (size_t)(m0 + rr) * K + k);
+    }
+  };
+  auto store_x_regs = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) xa[buf][threadIdx.x + 256 * j] = xr[j];
+  };
+#endif
+  auto load_x = [&](int st, int buf) {
+#pragma unroll
+    for (int j = 0; j < FRAGS / 4; ++j) {
+      const int f = wave * (FRAGS / 4) + j;
+      const int rr = min(16 * (f / STEPS) + l16, rows_left);
+      const int k = st * KS + 32 * (f % STEPS) + 8 * quad;
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(x + (size_t)(m0 + rr) * K + k),
+          (__attribute__((address_space(3))) void*)(&xa[buf][f * 64]), 16, 0, 0);
+    }
+  };
+
+  struct WRegs {
+    u32x4_t slot[NT];
+    uint32_t sc[NT][NGS];
+    uint32_t zw[NT];
+  };
+  auto load_w = [&](int st, WRegs& R) {
+    const int kb = (st * KS) / KB;
+    const int g0 = (st * KS) / GS;
+#pragma unroll
+    for (int s = 0; s < NT; ++s) {
+      R.slot[s] = Qt[((size_t)sidx[s] * nblk + kb) * 64 + lane];
+      const int n = 16 * sidx[s] + l16;
+#pragma unroll
+      for (int q = 0; q < NGS; ++q) R.sc[s][q] = scales[(size_t)(g0 + q) * N + n];
+      if constexpr (ZP) R.zw[s] = qz[(size_t)(g0 / PACK) * N + n];
+      else R.zw[s] = ZSYM;
+    }
+  };
+
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int s = 0; s < NT; ++s) acc[i][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  WRegs cur, nxt;
+  load_x(0, 0);
+  load_w(0, cur);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    // per-stage dequant constants of each group this stage touches
+    GroupConst gc[NT][NGS];
+    const int g0 = (st * KS) / GS;
+#pragma unroll
+    for (int s = 0; s < NT; ++s)
+#pragma unroll
+      for (int q = 0; q < NGS; ++q) {
+        const uint32_t sb = cur.sc[s][q] & 0xFFFFu;
+        const float sc = f16_bits_to_f32((uint16_t)sb);
+        const uint32_t z = (cur.zw[s] >> (((g0 + q) % PACK) * W_BIT)) & ((1u << W_BIT) - 1u);
+        const float zb = 1024.0f + (float)z;
+        gc[s][q].s = sc;
+        gc[s][q].zb_s = zb * sc;
+        gc[s][q].s_h2 = sb | (sb << 16);
+        const uint32_t nzb = __builtin_bit_cast(uint16_t, (_Float16)(-zb));
+        gc[s][q].nzb_h2 = nzb | (nzb << 16);
+      }
+    const u32x4_t* xs_buf = &xa[buf][0];
+    // B operands of this stage's first k step
+    const int sub = W_BIT == 2 ? (st & 1) : 0;  // int2: which half of the 256-deep block
+    u32x4_t b[NT], bn[NT];
+    // layout word of k step kk (int4: one word per step; int2: one per two)
+    auto word_of = [&](int s, int kk) {
+      return W_BIT == 4 ? cur.slot[s][kk] : cur.slot[s][(STEPS * sub + kk) >> 1];
+    };
+#pragma unroll
+    for (int s = 0; s < NT; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        b[s][t] = bpair_scaled<W_BIT, XDT>(word_of(s, 0), (STEPS * sub) & 1, t, gc[s][0]);
+    // everything of the current stage held in registers has been consumed
+    // or copied above, so no wait for it lands behind the prefetch below
+    __builtin_amdgcn_sched_barrier(0);
+
+    // prefetch the next stage (the last iteration re-reads the final stage
+    // into the idle buffer, keeping the loop body free of branches)
+    const int stn = min(st + 1, nst - 1);
+    // weights first: a wait the compiler may need on these registers must
+    // not also drain the x fragments (vmcnt retires loads in issue order)
+    load_w(stn, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+#if QMM_X_VIA_REGS
+    load_x_regs(stn);
+#else
+    load_x(stn, buf ^ 1);
+#endif
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Software pipeline inside the stage: while the NT MFMAs of row tile i of
+    // k step k run, (1) the A fragment two tiles ahead is read from LDS and
+    // (2) one operand register of k step k + 1's B fragments is dequantized
+    // (MT row tiles x 1 register = NT strips x 4 registers when MT = 16).
+    // The scheduling barriers hold this interleave; without them the
+    // compiler hoists every read and every conversion (and spills).
+    u32x4_t a0 = xs_buf[(0 * STEPS + 0) * 64 + lane];
+    u32x4_t a1 = xs_buf[(1 * STEPS + 0) * 64 + lane];
+#pragma unroll
+    for (int k = 0; k < STEPS; ++k) {
+      const int kn = k + 1;
+      const int qn = GS < KS ? (32 * kn) / GS : 0;
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const int t2 = k * MT + i + 2;  // fragment two ahead, in (k, i) order
+        u32x4_t an = a1;
+        if (t2 < STEPS * MT) an = xs_buf[((t2 % MT) * STEPS + t2 / MT) * 64 + lane];
+#pragma unroll
+        for (int s = 0; s < NT; ++s) mfma16_acc<XDT>(acc[i][s], a0, b[s]);
+        // operand registers of the next k step, spread over the row tiles
+        if (kn < STEPS) {
+#pragma unroll
+          for (int r = i * NT * 4 / MT; r < (i + 1) * NT * 4 / MT; ++r)
+            bn[r / 4][r % 4] = bpair_scaled<W_BIT, XDT>(word_of(r / 4, kn), (STEPS * sub + kn) & 1,
+                                                        r % 4, gc[r / 4][qn]);
+        }
+        a0 = a1;
+        a1 = an;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (kn < STEPS) {
+#pragma unroll
+        for (int s = 0; s < NT; ++s) b[s] = bn[s];
+      }
+    }
+    cur = nxt;
+#if QMM_X_VIA_REGS
+    store_x_regs(buf ^ 1);
+#endif
+    // the next stage's x tile was written to LDS by the memory pipeline:
+    // wait for this wave's loads, then for every wave's
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+  }
+  // the accumulators were last written by MFMAs the compiler does not see
+  // as such: give them their result latency before they are read
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+  for (int s = 0; s < NT; ++s) {
+    if (s0 + s >= strips) continue;
+    const int n = 16 * (s0 + s) + l16;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 16 * i + 4 * quad + r;
+        if (m < M) y[(size_t)m * N + n] = acc[i][s][r];
+      }
+  }
 }
 
 // ---------------------------------------------------------------- host side
-static void skinny_shape(int M, int w_bit, int* mt, int* nt) {
-  if (M <= 16) { *mt = 1; *nt = 4; }
-  else if (M <= 32) { *mt = 2; *nt = 4; }
-  else { *mt = 4; *nt = 2; }
-  (void)w_bit;
+static void skinny_shape(int M, int N, int* mt, int* nt) {
+  *mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  // 2 strips per workgroup keeps the grid near or above the CU count for
+  // the usual N; 1 strip when N is small
+  *nt = (N / 16 >= 512) ? 2 : 1;
+  const int want = env_int("QMM_SKINNY_NT");
+  if (want == 1 || want == 2 || want == 4) *nt = want;
 }
 
 GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size) {
   GemmPlan p{};
   (void)group_size;
+  const int big = env_int("QMM_GEMM_LARGE_MIN_M");
+  if (w_bit != 8 && M > (big > 0 ? big : 64) && K % 128 == 0) {
+    p.kind = 1;
+    p.mtile = 16 * large_mt();
+    p.n_tiles = (N / 16 + 15) / 16;
+    p.m_tiles = (M + p.mtile - 1) / p.mtile;
+    p.nt = 16;
+    p.workspace_bytes = 0;
+    return p;
+  }
   int mt, nt;
-  skinny_shape(M, w_bit, &mt, &nt);
+  skinny_shape(M, N, &mt, &nt);
   p.kind = 0;
   p.mtile = 16 * mt;
-  const int strips = N / 16;
-  p.n_tiles = (strips + 4 * nt - 1) / (4 * nt);
+  p.n_tiles = (N / 16 + nt - 1) / nt;
   p.m_tiles = (M + p.mtile - 1) / p.mtile;
-  const int ks_ext = w_bit == 2 ? 256 : 128;  // k per pipeline stage
-  const int nst = (K + ks_ext - 1) / ks_ext;
-  const long tiles = (long)p.n_tiles * p.m_tiles;
-  int ksplit = (int)((512 + tiles - 1) / tiles);
-  const int want = env_int("QMM_GEMM_KSPLIT");
-  if (want > 0) ksplit = want;
-  if (ksplit > nst) ksplit = nst;
-  if (ksplit < 1) ksplit = 1;
-  // every split gets at least one stage
-  const int per = (nst + ksplit - 1) / ksplit;
-  ksplit = (nst + per - 1) / per;
-  p.ksplit = ksplit;
+  p.nt = nt;
   p.workspace_bytes = 0;
-  if (ksplit > 1) {
-    const size_t tickets = ((size_t)tiles * 4 + 255) / 256 * 256;
-    p.workspace_bytes = tickets + (size_t)ksplit * M * N * sizeof(float);
-  }
+  (void)K;
   return p;
 }
 
 template <int W_BIT, int XDT, int GS, int MT, int NT>
 static hipError_t launch_skinny(const MatmulArgs& a, const GemmPlan& p) {
-  unsigned* ticket = nullptr;
-  float* part = nullptr;
-  if (p.ksplit > 1) {
-    ticket = reinterpret_cast<unsigned*>(a.workspace);
-    const size_t tickets = ((size_t)p.n_tiles * p.m_tiles * 4 + 255) / 256 * 256;
-    part = reinterpret_cast<float*>(reinterpret_cast<char*>(a.workspace) + tickets);
-  }
-  const long blocks = (long)p.n_tiles * p.m_tiles * p.ksplit;
-  hipLaunchKernelGGL((gemm_skinny_kernel<W_BIT, XDT, GS, MT, NT>), dim3((unsigned)blocks),
+  constexpr int DEPTH = MT >= 4 ? 2 : 3;
+  const long blocks = (long)p.n_tiles * p.m_tiles;
+  hipLaunchKernelGGL((gemm_skinny_kernel<W_BIT, XDT, GS, MT, NT, DEPTH>), dim3((unsigned)blocks),
                      dim3(256), 0, a.stream, reinterpret_cast<const uint16_t*>(a.x),
                      reinterpret_cast<const u32x4_t*>(a.Q), a.scales,
-                     reinterpret_cast<const uint32_t*>(a.zeros), a.y, part, ticket, a.M, a.N,
-                     a.K, p.ksplit, p.n_tiles);
+                     reinterpret_cast<const uint32_t*>(a.zeros), a.y, a.M, a.N, a.K, p.n_tiles);
   return hipGetLastError();
+}
+
+template <int W_BIT, int XDT, int GS, int MT>
+static hipError_t launch_nt(const MatmulArgs& a, const GemmPlan& p) {
+  switch (p.nt) {
+    case 1: return launch_skinny<W_BIT, XDT, GS, MT, 1>(a, p);
+    case 2: return launch_skinny<W_BIT, XDT, GS, MT, 2>(a, p);
+    case 4: return launch_skinny<W_BIT, XDT, GS, MT, 4>(a, p);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int W_BIT, int XDT, int GS>
 static hipError_t launch_mt(const MatmulArgs& a, const GemmPlan& p) {
   switch (p.mtile) {
-    case 16: return launch_skinny<W_BIT, XDT, GS, 1, 4>(a, p);
-    case 32: return launch_skinny<W_BIT, XDT, GS, 2, 4>(a, p);
-    case 64: return launch_skinny<W_BIT, XDT, GS, 4, 2>(a, p);
+    case 16: return launch_nt<W_BIT, XDT, GS, 1>(a, p);
+    case 32: return launch_nt<W_BIT, XDT, GS, 2>(a, p);
+    case 64: return launch_nt<W_BIT, XDT, GS, 4>(a, p);
   }
   return hipErrorInvalidValue;
 }
@@ -383,8 +685,45 @@ static hipError_t launch_gs(const MatmulArgs& a, const GemmPlan& p) {
   }
 }
 
+template <int W_BIT, int XDT, int GS, bool ZP, int MT>
+static hipError_t launch_large_mt(const MatmulArgs& a, const GemmPlan& p) {
+  hipLaunchKernelGGL((gemm_large_kernel<W_BIT, XDT, GS, ZP, MT>), dim3((unsigned)(p.n_tiles * p.m_tiles)),
+                     dim3(256), 0, a.stream, reinterpret_cast<const uint16_t*>(a.x),
+                     reinterpret_cast<const u32x4_t*>(a.Q),
+                     reinterpret_cast<const uint16_t*>(a.scales),
+                     reinterpret_cast<const uint32_t*>(a.zeros), a.y, a.M, a.N, a.K, p.n_tiles);
+  return hipGetLastError();
+}
+
+template <int W_BIT, int XDT, int GS, bool ZP>
+static hipError_t launch_large_k(const MatmulArgs& a, const GemmPlan& p) {
+  return p.mtile == 128 ? launch_large_mt<W_BIT, XDT, GS, ZP, 8>(a, p)
+                        : launch_large_mt<W_BIT, XDT, GS, ZP, 16>(a, p);
+}
+
+template <int W_BIT, int XDT, int GS>
+static hipError_t launch_large_z(const MatmulArgs& a, const GemmPlan& p) {
+  return a.zeros != nullptr ? launch_large_k<W_BIT, XDT, GS, true>(a, p)
+                            : launch_large_k<W_BIT, XDT, GS, false>(a, p);
+}
+
+template <int W_BIT, int XDT>
+static hipError_t launch_large(const MatmulArgs& a, const GemmPlan& p) {
+  switch (a.group_size) {
+    case 32: return launch_large_z<W_BIT, XDT, 32>(a, p);
+    case 64: return launch_large_z<W_BIT, XDT, 64>(a, p);
+    case 128: return launch_large_z<W_BIT, XDT, 128>(a, p);
+    case 256: return launch_large_z<W_BIT, XDT, 256>(a, p);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemm(const MatmulArgs& a, const GemmPlan& p) {
   const bool f16 = a.x_dtype == XF16;
+  if (p.kind == 1) {
+    if (a.w_bit == 4) return f16 ? launch_large<4, XF16>(a, p) : launch_large<4, XBF16>(a, p);
+    return f16 ? launch_large<2, XF16>(a, p) : launch_large<2, XBF16>(a, p);
+  }
   switch (a.w_bit) {
     case 4: return f16 ? launch_gs<4, XF16>(a, p) : launch_gs<4, XBF16>(a, p);
     case 2: return f16 ? launch_gs<2, XF16>(a, p) : launch_gs<2, XBF16>(a, p);

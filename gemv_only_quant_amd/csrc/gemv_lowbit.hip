@@ -223,7 +223,6 @@ GemvLowbitPlan plan_gemv_lowbit(int M, int N, int K, int w_bit, int group_size) 
   const int rows = K / pack;
   const int rpg = group_size / pack;  // packed rows per group (power of two)
   p.mb = m_bucket(M);
-  p.waves = 4;
   p.n_tiles = (N + 15) / 16;
   // rows per lane: a power of two dividing the group, no more than the 64
   // row-lanes need to cover K in one pass, and an x slice within 64 KiB
@@ -233,7 +232,6 @@ GemvLowbitPlan plan_gemv_lowbit(int M, int N, int K, int w_bit, int group_size) 
   const int want = env_int("QMM_GEMV_RL");
   if (want >= 2 && want <= rl && (rl % want) == 0) rl = want;
   p.rl = rl;
-  p.ksplit = 1;
   p.workspace_bytes = 0;
   return p;
 }

@@ -22,10 +22,8 @@ struct MatmulArgs {
 struct GemvLowbitPlan {
   int mb;        // M bucket (compiled row count >= M)
   int rl;        // packed rows per lane (divides group_size / pack)
-  int waves;     // waves per workgroup
-  int n_tiles;   // 64-column tiles
-  int ksplit;    // workgroups along K per tile
-  size_t workspace_bytes;
+  int n_tiles;   // 16-column workgroup tiles
+  size_t workspace_bytes;  // always 0: a workgroup owns its columns over all of K
 };
 GemvLowbitPlan plan_gemv_lowbit(int M, int N, int K, int w_bit, int group_size);
 hipError_t launch_gemv_lowbit(const MatmulArgs& a, const GemvLowbitPlan& p);
@@ -50,12 +48,12 @@ hipError_t launch_dequant(const void* Q, int layout, const void* scales, const v
 
 // ---- MFMA GEMM on the tile layout ---------------------------------------
 struct GemmPlan {
-  int kind;      // 0: skinny (registers-direct), 1: LDS-tiled
+  int kind;      // 0: skinny (registers-direct, K split over the waves), 1: large-M tiled
   int mtile;     // rows per M tile
-  int ksplit;
+  int nt;        // 16-column strips per workgroup (skinny)
   int n_tiles;
   int m_tiles;
-  size_t workspace_bytes;
+  size_t workspace_bytes;  // always 0 in this version: no kernel needs one
 };
 GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size);
 hipError_t launch_gemm(const MatmulArgs& a, const GemmPlan& p);

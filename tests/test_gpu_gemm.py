@@ -129,3 +129,49 @@ def test_gemm_full_size_sampled(name):
     ratio = assert_within_bound(y[ms, ns], y_ref, a_ref, name)
     assert np.all(np.isfinite(y))
     print(f"{name}: max err/bound {ratio:.3g}")
+
+
+# ------------------------------------------------ large-M (prefill) kernel
+LARGE = [  # M, N, K, w_bit, group, x_dtype, symmetric
+    (65, 16, 128, 4, 128, si.F16, False),      # one ragged 256-row tile, one strip
+    (256, 240, 1024, 4, 128, si.BF16, False),  # ragged strips in the last wave
+    (300, 272, 512, 4, 64, si.F16, True),      # ragged M tile and N tile
+    (512, 256, 2048, 4, 32, si.BF16, False),
+    (130, 64, 1024, 4, 256, si.BF16, False),
+    (257, 96, 512, 2, 64, si.BF16, False),
+    (128, 48, 1024, 2, 128, si.F16, True),
+    (96, 32, 768, 2, 32, si.F16, False),
+]
+
+
+@pytest.mark.parametrize("M,N,K,w_bit,gs,xdt,sym", LARGE)
+def test_gemm_large_within_bound(M, N, K, w_bit, gs, xdt, sym):
+    case = si.lowbit_case(M, N, K, w_bit, gs, xdt, sym, seed=7 + M + N * 3 + K + w_bit)
+    y = run_gemm(case)
+    y_ref, a_ref = oracle.qmm(*case.oracle_args())
+    assert_within_bound(y, y_ref, a_ref, f"gemm large w{w_bit} M{M} N{N} K{K}")
+
+
+@pytest.mark.parametrize("M,N,K,w_bit,gs,xdt,sym", [
+    (300, 48, 1024, 4, 128, si.BF16, False),
+    (260, 32, 2048, 2, 64, si.F16, False),
+    (128, 16, 512, 4, 32, si.BF16, True),
+])
+def test_gemm_large_exact_probe_bit_exact(M, N, K, w_bit, gs, xdt, sym):
+    """Power-of-two scales keep (q - z) * s exact in 16 bits, so the
+    pre-scaled operands and every summation order are exact."""
+    case = si.exact_lowbit_case(M, N, K, w_bit, gs, xdt, sym, seed=M + K)
+    y = run_gemm(case)
+    y_ref, _ = oracle.qmm(*case.oracle_args())
+    assert np.array_equal(y.astype(np.float64), y_ref)
+
+
+def test_gemm_large_one_hot_reproduces_weights():
+    M, N, K = 128, 64, 512
+    base = si.exact_lowbit_case(M, N, K, 4, 128, si.BF16, False, seed=42)
+    ks = [(37 * m) % K for m in range(M)]
+    case = si.one_hot(base, ks)
+    y = run_gemm(case)
+    W = oracle.dequant(case.np_Q(), case.np_scales(), case.np_zeros(), N, K, 4, 128)
+    for m, k in enumerate(ks):
+        assert np.array_equal(y[m], W[k]), (m, k)
