@@ -1,23 +1,26 @@
 """Benchmark of the weight-only quantized matmul on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
 
 A step is one call of the hot path on one batch of synthetic input already
 resident in HBM.  The headline workload is the int4 group-128 asymmetric
-decode GEMV (M=1, K=N=4096, fp16 x, fp32 accumulation) and `value` is its
+decode GEMV (M=1, K=N=4096, fp16 x, fp32 accumulation); `value` is its
 effective weight bandwidth (packed weights + scales + zeros per call / time).
+Every other workload is timed the same way and reported under "workloads";
+the prefill GEMM (M=4096) is reported in TFLOP/s under "prefill".
 
 Memory-bound calls rotate over a pool of weight copies (> 2 x the 256 MB
-Infinity Cache), so every call streams its weights from HBM.  The K timed
-calls are captured once in a HIP graph and replayed; HIP events on the
-launch stream bracket the replay.  The prefill MFMA workload (M=4096) is
-timed the same way and reported under "prefill".  The CPU baseline times the
-plain single-threaded oracle on the host (see "cpu_baseline.sample").
+Infinity Cache), so every call streams its weights from HBM.  The timed
+calls are captured once in a HIP graph and replayed, bracketed by HIP
+events on the launch stream.  The CPU baseline times the plain
+single-threaded oracle on the host ("cpu_baseline.sample").
 Prints one JSON line.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -25,11 +28,21 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
-MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
+MFMA_PEAK_TFLOPS = 2500.0       # MI355X dense fp16/bf16 matrix peak
 POOL_BYTES = 512 << 20          # weight pool for memory-bound workloads
 
 HEADLINE = "int4_g128_asym_gemv_m1_k4096_n4096"
-PREFILL = "int4_g128_asym_prefill_m4096_k4096_n11008"
+OTHERS = [  # (workload, entry)
+    ("int8_gemv_m1_k1024_n1024", "gemv"),
+    ("int8_skinny_m16_k4096_n14336", "gemm"),
+    ("int8_skinny_m32_k4096_n14336", "gemm"),
+    ("int8_skinny_m64_k4096_n14336", "gemm"),
+    ("int4_g128_sym_m16_k8192_n8192", "gemm"),
+]
+PREFILL = ["int4_g128_asym_prefill_m4096_k4096_n11008",
+           "int2_g64_asym_prefill_m4096_k4096_n11008"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
+CSRC = os.path.join(ROOT, "gemv_only_quant_amd", "csrc")
 
 
 def bytes_of(case):
@@ -42,16 +55,8 @@ def bytes_of(case):
     return w, w + io
 
 
-def make_call(qmm, d, y, ws, path, Q):
-    c = d
-    fn = qmm.qmm_gemv if path == "gemv" else qmm.qmm_gemm
-
-    def call():
-        fn(c.x, Q, c.scales, c.zeros, y, c.M, c.N, c.K, c.w_bit, c.group_size, workspace=ws)
-    return call
-
-
 def time_workload(name, steps, warmup, path):
+    """Average µs per call of `steps` graph-replayed calls (plus eager µs)."""
     import torch
     import gemv_only_quant_amd as qmm
     import synth_inputs as si
@@ -59,63 +64,77 @@ def time_workload(name, steps, warmup, path):
     case = si.workload(name)
     wbytes, tbytes = bytes_of(case)
     d = case.to("cuda")
-    Q = d.Q if path == "gemv" else qmm.pack(d.Q, case.N, case.K, case.w_bit)
-    copies = 1 if path == "gemm" and case.M >= 1024 else max(1, -(-POOL_BYTES // wbytes))
-    pool = []
-    for i in range(copies):
-        if i == 0:
-            pool.append((d, Q))
-        else:
-            di = si.Case(d.name, d.M, d.N, d.K, d.w_bit, d.group_size, d.x_dtype, d.x.clone(),
-                         d.Q, d.scales.clone(),
-                         None if d.zeros is None else d.zeros.clone())
-            pool.append((di, Q.clone()))
+    Q0 = d.Q if path == "gemv" else qmm.pack(d.Q, case.N, case.K, case.w_bit)
+    copies = 1 if case.M >= 1024 else max(1, -(-POOL_BYTES // wbytes))
+    pool = [(Q0, d.scales, d.zeros)]
+    for _ in range(copies - 1):
+        pool.append((Q0.clone(), d.scales.clone(), None if d.zeros is None else d.zeros.clone()))
     y = torch.empty((case.M, case.N), dtype=torch.float32, device="cuda")
     ws = qmm.workspace_for(case.M, case.N, case.K, case.w_bit, case.group_size, "cuda")
-    calls = [make_call(qmm, di, y, ws, path, Qi) for di, Qi in pool]
+    fn = qmm.qmm_gemv if path == "gemv" else qmm.qmm_gemm
+
+    def call(i):
+        Q, s, z = pool[i % copies]
+        fn(d.x, Q, s, z, y, case.M, case.N, case.K, case.w_bit, case.group_size, workspace=ws)
 
     for i in range(warmup):
-        calls[i % copies]()
+        call(i)
     torch.cuda.synchronize()
-
-    # eager timing (host launch per call)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n_eager = min(steps, 200)
     start.record()
     for i in range(n_eager):
-        calls[i % copies]()
+        call(i)
     end.record()
     torch.cuda.synchronize()
     eager_us = start.elapsed_time(end) * 1e3 / n_eager
 
-    # graph of exactly `steps` calls, replayed once untimed, then timed
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        calls[0]()
+        call(0)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
         for i in range(steps):
-            calls[i % copies]()
+            call(i)
     graph.replay()
     torch.cuda.synchronize()
     y_graph = y.clone()
-    calls[(steps - 1) % copies]()     # eager result of the same last call
+    call(steps - 1)  # eager result of the same last call
     torch.cuda.synchronize()
-    assert torch.equal(y_graph, y), "graph replay differs from eager call"
+    assert torch.equal(y_graph, y), f"{name}: graph replay differs from eager call"
 
     torch.cuda.synchronize()
     start.record()
     graph.replay()
     end.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end)
-    us = ms * 1e3 / steps
-    flops = 2.0 * case.M * case.N * case.K
-    return dict(case=case, us=us, ms_total=ms, eager_us=eager_us, wbytes=wbytes,
-                tbytes=tbytes, flops=flops, copies=copies)
+    us = start.elapsed_time(end) * 1e3 / steps
+    del graph, pool
+    return dict(case=case, us=us, eager_us=eager_us, wbytes=wbytes, tbytes=tbytes,
+                flops=2.0 * case.M * case.N * case.K, copies=copies)
+
+
+def traffic_for(name):
+    """HBM bytes per launch from the committed counter summary, if the kernel
+    source it was taken with is unchanged; else None."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    for m in re.finditer(r"^traffic_bytes_per_launch:\s+(\S+)\s+(\d+)\s+(\S+)\s+([0-9a-f]+)\s*$",
+                         text, re.M):
+        if m.group(1) != name:
+            continue
+        src = os.path.join(CSRC, m.group(3))
+        try:
+            h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        except OSError:
+            return None
+        return int(m.group(2)) if h == m.group(4) else None
+    return None
 
 
 def cpu_baseline(name, budget_s=10.0):
@@ -134,8 +153,20 @@ def cpu_baseline(name, budget_s=10.0):
             break
     t = el / reps
     return {"value": round(wbytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full {name} products (fp64 oracle, 1 thread), "
-                      f"{t:.3f} s each"}
+            "sample": f"{reps} full {name} products (fp64 oracle, 1 thread), {t:.3f} s each"}
+
+
+def line(r, path):
+    case, us = r["case"], r["us"]
+    out = {"workload": case.name, "entry": f"qmm_{path}", "us_per_call": round(us, 3),
+           "weight_GBps": round(r["wbytes"] / us / 1e3, 1),
+           "hbm_frac": round(r["tbytes"] / us / 1e3 / HBM_PEAK_GBS, 4),
+           "tflops": round(r["flops"] / us / 1e6, 2),
+           "mfma_frac": round(r["flops"] / us / 1e6 / MFMA_PEAK_TFLOPS, 4)}
+    t = traffic_for(case.name)
+    if t is not None:
+        out["traffic_bytes"] = t
+    return out
 
 
 def main():
@@ -144,28 +175,23 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--quick", action="store_true", help="headline only")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the kernels run on a single device; see the design notes on sharding)",
+              "(the kernels run on a single device; the design notes describe sharding)",
               file=sys.stderr)
         sys.exit(2)
 
     import torch
     import synth_inputs as si
     torch.cuda.set_device(0)
-    path = "gemv" if si.workload(args.workload).M <= 16 and args.workload.find("prefill") < 0 \
-        else "gemm"
-    r = time_workload(args.workload, args.steps, args.warmup, path)
-    case = r["case"]
-    us = r["us"]
-    value = r["wbytes"] / (us * 1e-6) / 1e9
+    r = time_workload(HEADLINE, args.steps, args.warmup, "gemv")
+    case, us = r["case"], r["us"]
     achieved = r["tbytes"] / (us * 1e-6) / 1e9
     out = {
         "metric": "effective weight GB/s @M=1 and TFLOP/s @M=4096, int4-g128 and int8 W-only",
-        "value": round(value, 2),
+        "value": round(r["wbytes"] / (us * 1e-6) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -176,26 +202,27 @@ def main():
         "vs_baseline": None,
         "dtype": "f16" if case.x_dtype == si.F16 else "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "M": case.M, "N": case.N, "K": case.K,
+        "config": {"workload": HEADLINE, "M": case.M, "N": case.N, "K": case.K,
                    "w_bit": case.w_bit, "group_size": case.group_size,
-                   "zeros": case.zeros is not None, "accumulate": "f32", "entry": f"qmm_{path}",
+                   "zeros": case.zeros is not None, "accumulate": "f32", "entry": "qmm_gemv",
                    "weight_pool_copies": r["copies"], "timing": "hip graph replay",
                    "eager_us_per_call": round(r["eager_us"], 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": traffic_for(HEADLINE)},
     }
-    if not args.no_prefill:
-        try:
-            p = time_workload(PREFILL, 20, 3, "gemm")
+    if not args.quick:
+        out["workloads"] = [line(time_workload(n, 200, 20, p), p) for n, p in OTHERS]
+        pre = []
+        for n in PREFILL:
+            p = time_workload(n, 10, 3, "gemm")
             tf = p["flops"] / (p["us"] * 1e-6) / 1e12
-            out["prefill"] = {"workload": PREFILL, "us_per_call": round(p["us"], 2),
-                              "tflops": round(tf, 2), "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
-                              "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
-        except Exception as e:  # the MFMA path may not support this shape yet
-            out["prefill"] = {"workload": PREFILL, "error": str(e)[:200]}
+            pre.append({"workload": n, "entry": "qmm_gemm", "us_per_call": round(p["us"], 2),
+                        "tflops": round(tf, 2), "peak_tflops": MFMA_PEAK_TFLOPS,
+                        "frac": round(tf / MFMA_PEAK_TFLOPS, 4)})
+        out["prefill"] = pre
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(args.workload)
+        out["cpu_baseline"] = cpu_baseline(HEADLINE)
     print(json.dumps(out), flush=True)
 
 

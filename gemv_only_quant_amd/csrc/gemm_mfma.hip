@@ -607,9 +607,10 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
 // ---------------------------------------------------------------- host side
 static void skinny_shape(int M, int N, int* mt, int* nt) {
   *mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  // 2 strips per workgroup keeps the grid near or above the CU count for
-  // the usual N; 1 strip when N is small
-  *nt = (N / 16 >= 512) ? 2 : 1;
+  // widest strip count (more x reuse per wave) that still leaves about as
+  // many workgroups as CUs (measured: 4 strips at N = 14336, 2 at N = 8192)
+  const int strips = N / 16;
+  *nt = strips / 4 >= 192 ? 4 : (strips / 2 >= 192 ? 2 : 1);
   const int want = env_int("QMM_SKINNY_NT");
   if (want == 1 || want == 2 || want == 4) *nt = want;
 }
