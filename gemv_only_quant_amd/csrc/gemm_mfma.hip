@@ -390,7 +390,7 @@ template <int W_BIT, int XDT, int GS, bool ZP, int MT>
 __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ Qt,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qz, float* __restrict__ y,
-    int M, int N, int K, int n_tiles) {
+    int M, int N, int K, int n_tiles, int rot_mod, int rot_step) {
   constexpr int BM = 16 * MT;          // rows per workgroup (MT 16-row tiles)
   constexpr int NT = 4;                 // strips per wave
   constexpr int KS = 128;               // k per stage
@@ -414,6 +414,13 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
   const int s0 = (nt * 4 + wave) * NT;
   const int nblk = K / KB;
   const int nst = K / KS;
+  // Workgroups start their K loop at different stages: the workgroups that
+  // run at the same time on one XCD share x rows and a k range, and rows
+  // K * 2 bytes apart all fall on the same few L2 channels.  Rotating the
+  // start by the N-tile index spreads their loads over the channels (the
+  // fp32 sums of a tile still follow one fixed order).
+  const int rot = ((nt % rot_mod) * rot_step) % nst;
+  auto stage_of = [&](int i) { const int v = i + rot; return v >= nst ? v - nst : v; };
 
   // Loads always use a valid strip (the last one stands in for strips past
   // N); their results are simply not stored.
@@ -428,26 +435,6 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
   // bytes land at block + 16 p).  Rows past M read row M - 1 instead: they
   // only feed output rows that are never stored.
   const int rows_left = M - 1 - m0;
-#if QMM_X_VIA_REGS
-  // x chunk c = threadIdx + 256 j of a stage is fragment c / 64, lane c % 64:
-  // loaded into registers at the start of a stage, written to LDS at its end
-  constexpr int XPT = FRAGS * 64 / 256;
-  u32x4_t xr[XPT];
-  auto load_x_regs = [&](int st) {
-#pragma unroll
-    for (int j = 0; j < XPT; ++j) {
-      const int c = threadIdx.x + 256 * j;
-      const int f = c >> 6, p = c & 63;
-      const int rr = min(16 * (f / STEPS) + (p & 15), rows_left);
-      const int k = st * KS + 32 * (f % STEPS) + 8 * (p >> 4);
-      xr[j] = *reinterpret_cast<const u32x4_t*>(x + (size_t)(m0 + rr) * K + k);
-    }
-  };
-  auto store_x_regs = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < XPT; ++j) xa[buf][threadIdx.x + 256 * j] = xr[j];
-  };
-#endif
   auto load_x = [&](int st, int buf) {
 #pragma unroll
     for (int j = 0; j < FRAGS / 4; ++j) {
@@ -478,6 +465,34 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
       else R.zw[s] = ZSYM;
     }
   };
+  // Loads issued during a stage, one at a time: j < NWL are weight-side
+  // (slots, then scales, then zero words) of stage sw, the rest this wave's
+  // x fragments of stage sx.  The k loop issues them spread over its row
+  // tiles: a wave issues in order, so a burst of loads at the top of a stage
+  // would hold its MFMAs back until the memory pipeline had taken them all.
+  constexpr int NWL = NT * (2 + NGS);
+  constexpr int NLD = NWL + FRAGS / 4;
+  auto load_part = [&](int j, int sw, int sx, int buf, WRegs& R) {
+    const int kb = (sw * KS) / KB;
+    const int g0 = (sw * KS) / GS;
+    if (j < NT) {
+      R.slot[j] = Qt[((size_t)sidx[j] * nblk + kb) * 64 + lane];
+    } else if (j < NT + NT * NGS) {
+      const int s = (j - NT) / NGS, q = (j - NT) % NGS;
+      R.sc[s][q] = scales[(size_t)(g0 + q) * N + 16 * sidx[s] + l16];
+    } else if (j < NWL) {
+      const int s = j - NT - NT * NGS;
+      if constexpr (ZP) R.zw[s] = qz[(size_t)(g0 / PACK) * N + 16 * sidx[s] + l16];
+      else R.zw[s] = ZSYM;
+    } else {
+      const int f = wave * (FRAGS / 4) + (j - NWL);
+      const int rr = min(16 * (f / STEPS) + l16, rows_left);
+      const int k = sx * KS + 32 * (f % STEPS) + 8 * quad;
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(x + (size_t)(m0 + rr) * K + k),
+          (__attribute__((address_space(3))) void*)(&xa[buf][f * 64]), 16, 0, 0);
+    }
+  };
 
   f32x4_t acc[MT][NT];
 #pragma unroll
@@ -485,65 +500,87 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
 #pragma unroll
     for (int s = 0; s < NT; ++s) acc[i][s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  WRegs cur, nxt;
-  load_x(0, 0);
-  load_w(0, cur);
+  // dequant constants of strip s for each group of the stage at K position
+  // sa, from that stage's scale and zero words
+  auto group_consts = [&](const WRegs& R, int sa, int s, GroupConst (&g)[NGS]) {
+    const int g0 = (sa * KS) / GS;
+#pragma unroll
+    for (int q = 0; q < NGS; ++q) {
+      const uint32_t sb = R.sc[s][q] & 0xFFFFu;
+      const float sc = f16_bits_to_f32((uint16_t)sb);
+      const uint32_t z = (R.zw[s] >> (((g0 + q) % PACK) * W_BIT)) & ((1u << W_BIT) - 1u);
+      const float zb = 1024.0f + (float)z;
+      g[q].s = sc;
+      g[q].zb_s = zb * sc;
+      g[q].s_h2 = sb | (sb << 16);
+      const uint32_t nzb = __builtin_bit_cast(uint16_t, (_Float16)(-zb));
+      g[q].nzb_h2 = nzb | (nzb << 16);
+    }
+  };
+  // layout word of k step kk of a stage (int4: one word per step; int2: one
+  // per two steps, the stage being half `sub` of a 256-deep block)
+  auto word_of = [&](const WRegs& R, int s, int sub, int kk) {
+    return W_BIT == 4 ? R.slot[s][kk] : R.slot[s][(STEPS * sub + kk) >> 1];
+  };
+
+  // Weight registers of three stages: the current one, the next (loaded
+  // during the previous stage) and the one after (loading now).  The x
+  // tile of the next stage goes straight to LDS, and while such a load is
+  // in flight the compiler can only wait for every earlier load (vmcnt 0):
+  // loading weights two stages ahead lets the last k step read the next
+  // stage's weights, complete since the previous stage's closing wait.
+  WRegs cur, nx1, nx2;
+  load_x(stage_of(0), 0);
+  load_w(stage_of(0), cur);
+  load_w(stage_of(min(1, nst - 1)), nx1);
+  // pin the loads above the wait (the compiler may otherwise sink them
+  // into the loop preheader, where they would still be in flight)
+  auto pin = [](const WRegs& R) {
+#pragma unroll
+    for (int s = 0; s < NT; ++s) {
+      asm volatile("" ::"v"(R.slot[s]), "v"(R.zw[s]));
+#pragma unroll
+      for (int q = 0; q < NGS; ++q) asm volatile("" ::"v"(R.sc[s][q]));
+    }
+  };
+  pin(cur);
+  pin(nx1);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    // per-stage dequant constants of each group this stage touches
-    GroupConst gc[NT][NGS];
-    const int g0 = (st * KS) / GS;
+  // The first stage's group constants and first B fragment are made here;
+  // from then on each stage makes the next one's during its last k step,
+  // so a stage opens straight into its MFMAs.
+  GroupConst gc[NT][NGS], gcn[NT][NGS];
+  u32x4_t b[NT], bn[NT];
+  {
+    const int sa = stage_of(0);
+    const int sub = W_BIT == 2 ? (sa & 1) : 0;
 #pragma unroll
-    for (int s = 0; s < NT; ++s)
-#pragma unroll
-      for (int q = 0; q < NGS; ++q) {
-        const uint32_t sb = cur.sc[s][q] & 0xFFFFu;
-        const float sc = f16_bits_to_f32((uint16_t)sb);
-        const uint32_t z = (cur.zw[s] >> (((g0 + q) % PACK) * W_BIT)) & ((1u << W_BIT) - 1u);
-        const float zb = 1024.0f + (float)z;
-        gc[s][q].s = sc;
-        gc[s][q].zb_s = zb * sc;
-        gc[s][q].s_h2 = sb | (sb << 16);
-        const uint32_t nzb = __builtin_bit_cast(uint16_t, (_Float16)(-zb));
-        gc[s][q].nzb_h2 = nzb | (nzb << 16);
-      }
-    const u32x4_t* xs_buf = &xa[buf][0];
-    // B operands of this stage's first k step
-    const int sub = W_BIT == 2 ? (st & 1) : 0;  // int2: which half of the 256-deep block
-    u32x4_t b[NT], bn[NT];
-    // layout word of k step kk (int4: one word per step; int2: one per two)
-    auto word_of = [&](int s, int kk) {
-      return W_BIT == 4 ? cur.slot[s][kk] : cur.slot[s][(STEPS * sub + kk) >> 1];
-    };
-#pragma unroll
-    for (int s = 0; s < NT; ++s)
+    for (int s = 0; s < NT; ++s) {
+      group_consts(cur, sa, s, gc[s]);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
-        b[s][t] = bpair_scaled<W_BIT, XDT>(word_of(s, 0), (STEPS * sub) & 1, t, gc[s][0]);
-    // everything of the current stage held in registers has been consumed
-    // or copied above, so no wait for it lands behind the prefetch below
-    __builtin_amdgcn_sched_barrier(0);
-
-    // prefetch the next stage (the last iteration re-reads the final stage
-    // into the idle buffer, keeping the loop body free of branches)
-    const int stn = min(st + 1, nst - 1);
-    // weights first: a wait the compiler may need on these registers must
-    // not also drain the x fragments (vmcnt retires loads in issue order)
-    load_w(stn, nxt);
-    __builtin_amdgcn_sched_barrier(0);
-#if QMM_X_VIA_REGS
-    load_x_regs(stn);
-#else
-    load_x(stn, buf ^ 1);
-#endif
-    __builtin_amdgcn_sched_barrier(0);
+        b[s][t] = bpair_scaled<W_BIT, XDT>(word_of(cur, s, sub, 0), (STEPS * sub) & 1, t, gc[s][0]);
+    }
+  }
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    const int sa = stage_of(st);  // the stage's place along K
+    const int sub = W_BIT == 2 ? (sa & 1) : 0;  // int2: which half of the 256-deep block
+    // the next stage, loaded during this one (the last iteration re-reads
+    // the final stage into the idle buffer, keeping the loop free of
+    // branches)
+    const int stn = stage_of(min(st + 1, nst - 1));
+    const int stw = stage_of(min(st + 2, nst - 1));  // weights loaded now
+    const int subn = W_BIT == 2 ? (stn & 1) : 0;
+    const u32x4_t* xs_buf = &xa[buf][0];
 
     // Software pipeline inside the stage: while the NT MFMAs of row tile i of
-    // k step k run, (1) the A fragment two tiles ahead is read from LDS and
-    // (2) one operand register of k step k + 1's B fragments is dequantized
-    // (MT row tiles x 1 register = NT strips x 4 registers when MT = 16).
+    // k step k run, (1) the A fragment two tiles ahead is read from LDS,
+    // (2) one operand register of the next k step's B fragments is
+    // dequantized (MT row tiles x 1 register = NT strips x 4 registers when
+    // MT = 16) -- in the last k step those of the next stage, after its
+    // group constants -- and (3) part of the next stage's loads is issued.
     // The scheduling barriers hold this interleave; without them the
     // compiler hoists every read and every conversion (and spills).
     u32x4_t a0 = xs_buf[(0 * STEPS + 0) * 64 + lane];
@@ -559,26 +596,42 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
         if (t2 < STEPS * MT) an = xs_buf[((t2 % MT) * STEPS + t2 / MT) * 64 + lane];
 #pragma unroll
         for (int s = 0; s < NT; ++s) mfma16_acc<XDT>(acc[i][s], a0, b[s]);
-        // operand registers of the next k step, spread over the row tiles
         if (kn < STEPS) {
 #pragma unroll
           for (int r = i * NT * 4 / MT; r < (i + 1) * NT * 4 / MT; ++r)
-            bn[r / 4][r % 4] = bpair_scaled<W_BIT, XDT>(word_of(r / 4, kn), (STEPS * sub + kn) & 1,
-                                                        r % 4, gc[r / 4][qn]);
+            bn[r / 4][r % 4] = bpair_scaled<W_BIT, XDT>(word_of(cur, r / 4, sub, kn),
+                                                        (STEPS * sub + kn) & 1, r % 4, gc[r / 4][qn]);
+        } else {
+          if (i < NT) group_consts(nx1, stn, i, gcn[i]);
+#pragma unroll
+          for (int r = i * NT * 4 / MT; r < (i + 1) * NT * 4 / MT; ++r)
+            bn[r / 4][r % 4] = bpair_scaled<W_BIT, XDT>(word_of(nx1, r / 4, subn, 0),
+                                                        (STEPS * subn) & 1, r % 4, gcn[r / 4][0]);
+        }
+        // this row tile's share of the loads, spread over the first 7/8 of
+        // the row tiles
+        {
+          constexpr int S7 = 7 * STEPS * MT / 8;
+          static_assert(NLD <= 2 * S7, "two loads per row tile at most");
+          const int p = k * MT + i;
+          const int j0 = (p * NLD + S7 - 1) / S7;
+          const int j1 = min(NLD, ((p + 1) * NLD + S7 - 1) / S7);
+          if (j0 < j1) load_part(j0, stw, stn, buf ^ 1, nx2);
+          if (j0 + 1 < j1) load_part(j0 + 1, stw, stn, buf ^ 1, nx2);
         }
         a0 = a1;
         a1 = an;
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (kn < STEPS) {
 #pragma unroll
-        for (int s = 0; s < NT; ++s) b[s] = bn[s];
-      }
+      for (int s = 0; s < NT; ++s) b[s] = bn[s];
     }
-    cur = nxt;
-#if QMM_X_VIA_REGS
-    store_x_regs(buf ^ 1);
-#endif
+    cur = nx1;
+    nx1 = nx2;
+#pragma unroll
+    for (int s = 0; s < NT; ++s)
+#pragma unroll
+      for (int q = 0; q < NGS; ++q) gc[s][q] = gcn[s][q];
     // the next stage's x tile was written to LDS by the memory pipeline:
     // wait for this wave's loads, then for every wave's
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -688,11 +741,15 @@ static hipError_t launch_gs(const MatmulArgs& a, const GemmPlan& p) {
 
 template <int W_BIT, int XDT, int GS, bool ZP, int MT>
 static hipError_t launch_large_mt(const MatmulArgs& a, const GemmPlan& p) {
+  // start-stage rotation: N tile t starts at stage (t % rot_mod) * rot_step
+  const int er = env_int("QMM_ROT_MOD"), es = env_int("QMM_ROT_STEP");
+  const int rot_mod = er >= 1 ? er : 8, rot_step = es >= 0 ? es : 1;
   hipLaunchKernelGGL((gemm_large_kernel<W_BIT, XDT, GS, ZP, MT>), dim3((unsigned)(p.n_tiles * p.m_tiles)),
                      dim3(256), 0, a.stream, reinterpret_cast<const uint16_t*>(a.x),
                      reinterpret_cast<const u32x4_t*>(a.Q),
                      reinterpret_cast<const uint16_t*>(a.scales),
-                     reinterpret_cast<const uint32_t*>(a.zeros), a.y, a.M, a.N, a.K, p.n_tiles);
+                     reinterpret_cast<const uint32_t*>(a.zeros), a.y, a.M, a.N, a.K, p.n_tiles,
+                     rot_mod, rot_step);
   return hipGetLastError();
 }
 
