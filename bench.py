@@ -11,16 +11,20 @@ the prefill GEMM (M=4096) is reported in TFLOP/s under "prefill".
 
 Memory-bound calls rotate over a pool of weight copies (> 2 x the 256 MB
 Infinity Cache), so every call streams its weights from HBM.  The timed
-calls are captured once in a HIP graph and replayed, bracketed by HIP
-events on the launch stream.  The CPU baseline times the plain
-single-threaded oracle on the host ("cpu_baseline.sample").
-Prints one JSON line.
+calls are captured once in a HIP graph and replayed five times, each replay
+bracketed by HIP events on the launch stream; the median replay gives the
+time per call.  "calibration" holds what this GPU reaches on plain work of
+the same kind (a device-to-device copy, the vendor BLAS's dense bf16 GEMM
+of the prefill shape), labelled as such; the roofline peaks stay the
+published ones.  The CPU baseline times the plain single-threaded oracle on
+the host ("cpu_baseline.sample").  Prints one JSON line.
 """
 import argparse
 import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -106,15 +110,59 @@ def time_workload(name, steps, warmup, path):
     torch.cuda.synchronize()
     assert torch.equal(y_graph, y), f"{name}: graph replay differs from eager call"
 
-    torch.cuda.synchronize()
-    start.record()
-    graph.replay()
-    end.record()
-    torch.cuda.synchronize()
-    us = start.elapsed_time(end) * 1e3 / steps
+    reps = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        start.record()
+        graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        reps.append(start.elapsed_time(end) * 1e3 / steps)
+    us = statistics.median(reps)
     del graph, pool
     return dict(case=case, us=us, eager_us=eager_us, wbytes=wbytes, tbytes=tbytes,
                 flops=2.0 * case.M * case.N * case.K, copies=copies)
+
+
+def calibration():
+    """What this GPU reaches on plain work: a 1 GiB device-to-device copy
+    (read + write bytes / time) and torch's dense bf16 GEMM (vendor BLAS) at
+    M=4096, K=4096, N=11008 with fp32 output."""
+    import torch
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    src = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    copy_us = timed(lambda: dst.copy_(src), 20)
+    del src, dst
+    g = torch.Generator(device="cuda").manual_seed(0)
+    M, K, N = 4096, 4096, 11008
+    a = torch.randn((M, K), device="cuda", dtype=torch.bfloat16, generator=g)
+    w = torch.randn((K, N), device="cuda", dtype=torch.bfloat16, generator=g)
+    try:
+        out_dt = "f32"
+        gemm_us = timed(lambda: torch.mm(a, w, out_dtype=torch.float32), 20)
+    except (RuntimeError, TypeError):
+        out_dt = "bf16"
+        gemm_us = timed(lambda: torch.mm(a, w), 20)
+    return {"hbm_copy_GBps": round(2 * (1 << 30) / copy_us / 1e3, 1),
+            "dense_bf16_gemm_m4096_k4096_n11008_us": round(gemm_us, 1),
+            "dense_bf16_gemm_tflops": round(2 * M * N * K / gemm_us / 1e6, 1),
+            "dense_gemm_out_dtype": out_dt,
+            "note": "measured here on plain work, for context; roofline peaks are the published ones"}
 
 
 def traffic_for(name):
@@ -221,6 +269,7 @@ def main():
                         "tflops": round(tf, 2), "peak_tflops": MFMA_PEAK_TFLOPS,
                         "frac": round(tf / MFMA_PEAK_TFLOPS, 4)})
         out["prefill"] = pre
+        out["calibration"] = calibration()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(HEADLINE)
     print(json.dumps(out), flush=True)

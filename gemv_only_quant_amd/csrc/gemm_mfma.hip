@@ -2,10 +2,14 @@
 // layout written by qmm_pack (repack.hip), on v_mfma_f32_16x16x32_{f16,bf16}.
 //
 // Skinny kernel (decode batches, M up to a few 16-row tiles), HBM-bound:
-//  * a workgroup = 4 waves on one M-tile and one K-range; each wave owns NT
-//    16-column strips.  Per stage (128 k; 256 k for int2) a lane loads ONE
-//    16-byte slot of each strip's 1 KiB layout block -- already the MFMA
-//    B-operand lane map -- so weights go HBM -> VGPR -> MFMA without LDS;
+//  * a workgroup = 4 waves on one M-tile (MT 16-row tiles) and NT 16-column
+//    strips; the 4 waves split K into quarters, and their partial tiles meet
+//    in LDS at the end, so no partial sum leaves the workgroup;
+//  * per stage (128 k; 256 k for int2; two 64-deep blocks for int8) a lane
+//    loads ONE 16-byte slot of each strip's 1 KiB layout block -- already
+//    the MFMA B-operand lane map -- so weights go HBM -> VGPR -> MFMA
+//    without LDS, and its x operand fragments straight from global memory;
+//    a DEPTH-deep ring of stages in registers keeps the loads in flight;
 //  * codes become operand pairs (B + q_a, B + q_b) with one mask-or per pair
 //    (fp16 B = 1024, bf16 B = 128; int8: u = q + 128 through a byte perm
 //    (fp16) or byte->float->bf16 converts (bf16)), exact in 16 bits;
@@ -13,13 +17,7 @@
 //    over the same k, in the accumulator layout; at each group end
 //        y += s * (acc - (B + z) * xsum)
 //    in fp32 -- so the matrix cores only see exact integers and the group
-//    scale is applied once per group (the page's w = (q - z) * s, regrouped);
-//  * the x tile of a stage goes through double-buffered LDS (ds_read does
-//    not wait on the in-order weight loads); weights, scales and zeros of
-//    stage i + 1 are in flight while stage i computes;
-//  * K is split over workgroups when the tile grid is small; partial tiles
-//    meet in the workspace and the last workgroup to arrive adds them in a
-//    fixed order and re-arms the ticket.
+//    scale is applied once per group (the page's w = (q - z) * s, regrouped).
 #include "qmm_device.h"
 #include "qmm_internal.h"
 
@@ -390,7 +388,7 @@ template <int W_BIT, int XDT, int GS, bool ZP, int MT>
 __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ Qt,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qz, float* __restrict__ y,
-    int M, int N, int K, int n_tiles, int rot_mod, int rot_step) {
+    int M, int N, int K, int n_tiles) {
   constexpr int BM = 16 * MT;          // rows per workgroup (MT 16-row tiles)
   constexpr int NT = 4;                 // strips per wave
   constexpr int KS = 128;               // k per stage
@@ -414,13 +412,6 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
   const int s0 = (nt * 4 + wave) * NT;
   const int nblk = K / KB;
   const int nst = K / KS;
-  // Workgroups start their K loop at different stages: the workgroups that
-  // run at the same time on one XCD share x rows and a k range, and rows
-  // K * 2 bytes apart all fall on the same few L2 channels.  Rotating the
-  // start by the N-tile index spreads their loads over the channels (the
-  // fp32 sums of a tile still follow one fixed order).
-  const int rot = ((nt % rot_mod) * rot_step) % nst;
-  auto stage_of = [&](int i) { const int v = i + rot; return v >= nst ? v - nst : v; };
 
   // Loads always use a valid strip (the last one stands in for strips past
   // N); their results are simply not stored.
@@ -530,9 +521,9 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
   // loading weights two stages ahead lets the last k step read the next
   // stage's weights, complete since the previous stage's closing wait.
   WRegs cur, nx1, nx2;
-  load_x(stage_of(0), 0);
-  load_w(stage_of(0), cur);
-  load_w(stage_of(min(1, nst - 1)), nx1);
+  load_x(0, 0);
+  load_w(0, cur);
+  load_w(min(1, nst - 1), nx1);
   // pin the loads above the wait (the compiler may otherwise sink them
   // into the loop preheader, where they would still be in flight)
   auto pin = [](const WRegs& R) {
@@ -552,26 +543,20 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
   // so a stage opens straight into its MFMAs.
   GroupConst gc[NT][NGS], gcn[NT][NGS];
   u32x4_t b[NT], bn[NT];
-  {
-    const int sa = stage_of(0);
-    const int sub = W_BIT == 2 ? (sa & 1) : 0;
 #pragma unroll
-    for (int s = 0; s < NT; ++s) {
-      group_consts(cur, sa, s, gc[s]);
+  for (int s = 0; s < NT; ++s) {
+    group_consts(cur, 0, s, gc[s]);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        b[s][t] = bpair_scaled<W_BIT, XDT>(word_of(cur, s, sub, 0), (STEPS * sub) & 1, t, gc[s][0]);
-    }
+    for (int t = 0; t < 4; ++t) b[s][t] = bpair_scaled<W_BIT, XDT>(word_of(cur, s, 0, 0), 0, t, gc[s][0]);
   }
   for (int st = 0; st < nst; ++st) {
     const int buf = st & 1;
-    const int sa = stage_of(st);  // the stage's place along K
-    const int sub = W_BIT == 2 ? (sa & 1) : 0;  // int2: which half of the 256-deep block
+    const int sub = W_BIT == 2 ? (st & 1) : 0;  // int2: which half of the 256-deep block
     // the next stage, loaded during this one (the last iteration re-reads
     // the final stage into the idle buffer, keeping the loop free of
     // branches)
-    const int stn = stage_of(min(st + 1, nst - 1));
-    const int stw = stage_of(min(st + 2, nst - 1));  // weights loaded now
+    const int stn = min(st + 1, nst - 1);
+    const int stw = min(st + 2, nst - 1);  // weights loaded now
     const int subn = W_BIT == 2 ? (stn & 1) : 0;
     const u32x4_t* xs_buf = &xa[buf][0];
 
@@ -741,15 +726,11 @@ static hipError_t launch_gs(const MatmulArgs& a, const GemmPlan& p) {
 
 template <int W_BIT, int XDT, int GS, bool ZP, int MT>
 static hipError_t launch_large_mt(const MatmulArgs& a, const GemmPlan& p) {
-  // start-stage rotation: N tile t starts at stage (t % rot_mod) * rot_step
-  const int er = env_int("QMM_ROT_MOD"), es = env_int("QMM_ROT_STEP");
-  const int rot_mod = er >= 1 ? er : 8, rot_step = es >= 0 ? es : 1;
   hipLaunchKernelGGL((gemm_large_kernel<W_BIT, XDT, GS, ZP, MT>), dim3((unsigned)(p.n_tiles * p.m_tiles)),
                      dim3(256), 0, a.stream, reinterpret_cast<const uint16_t*>(a.x),
                      reinterpret_cast<const u32x4_t*>(a.Q),
                      reinterpret_cast<const uint16_t*>(a.scales),
-                     reinterpret_cast<const uint32_t*>(a.zeros), a.y, a.M, a.N, a.K, p.n_tiles,
-                     rot_mod, rot_step);
+                     reinterpret_cast<const uint32_t*>(a.zeros), a.y, a.M, a.N, a.K, p.n_tiles);
   return hipGetLastError();
 }
 

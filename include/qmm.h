@@ -106,13 +106,14 @@ QMM_API qmm_status qmm_unpack_layout(const void* Q_mfma, void* Q_canon, int N, i
                              void* stream);
 
 /*
- * Workspace for qmm_gemv / qmm_gemm (split-K partial sums and arrival
- * counters).  Caller-owned device memory of at least
- * qmm_workspace_bytes(...) bytes, ZERO-FILLED ONCE when allocated; every
- * call leaves its counters at zero again, so one workspace serves any
- * number of successive calls on one stream.  Calls that may run
- * concurrently need distinct workspaces.  The size covers both entry
- * points for the given shape; it may be 0 (workspace may then be NULL).
+ * Scratch device memory that qmm_gemv / qmm_gemm need for the given shape
+ * beyond their inputs and outputs (cf. the lock workspace Marlin's
+ * marlin_cuda() takes from its caller).  The kernels of this version keep
+ * every partial sum inside a workgroup, so the size is 0 for every shape
+ * and the workspace argument may be NULL; a nonzero size, if a later
+ * scheduler needs one, is caller-owned memory of at least that many bytes,
+ * 16-byte aligned, and calls that may run concurrently would need distinct
+ * workspaces.  Returns 0 for invalid arguments too.
  */
 QMM_API size_t qmm_workspace_bytes(int M, int N, int K, int w_bit, int group_size);
 
