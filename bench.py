@@ -42,6 +42,7 @@ OTHERS = [  # (workload, entry)
     ("int8_skinny_m32_k4096_n14336", "gemm"),
     ("int8_skinny_m64_k4096_n14336", "gemm"),
     ("int4_g128_sym_m16_k8192_n8192", "gemm"),
+    ("int4_g128_asym_smalln_m16_k14336_n1024", "gemm"),  # 64 tiles: 8 waves each
 ]
 PREFILL = ["int4_g128_asym_prefill_m4096_k4096_n11008",
            "int2_g64_asym_prefill_m4096_k4096_n11008"]

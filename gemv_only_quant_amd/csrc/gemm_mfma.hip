@@ -84,12 +84,11 @@ __device__ __forceinline__ u32x4_t bfrag(const u32x4_t* slot, int st) {
   return b;
 }
 
-template <int W_BIT, int XDT, int GS, int MT, int NT, int DEPTH>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(
+template <int W_BIT, int XDT, int GS, int MT, int NT, int DEPTH, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ Qt,
     const void* __restrict__ scales, const uint32_t* __restrict__ qz, float* __restrict__ y,
     int M, int N, int K, int n_tiles) {
-  constexpr int WAVES = 4;
   constexpr int KB = Stage<W_BIT>::KB;
   constexpr int BLK = Stage<W_BIT>::BLK;
   constexpr int KS = KB * BLK;           // k per stage
@@ -111,7 +110,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
   const int s0 = nt * NT;
   const int nblk = K / KB;
   const int nst = (nblk + BLK - 1) / BLK;  // stages along K
-  // this wave's quarter of the stages
+  // this wave's share of the stages
   const int per = (nst + WAVES - 1) / WAVES;
   const int st0 = min(nst, wave * per);
   const int st1 = min(nst, st0 + per);
@@ -241,9 +240,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
     flush(sc, bz);
   }
 
-  // ---- the 4 K-quarters meet in LDS ------------------------------------
+  // ---- the waves' K ranges meet in LDS -----------------------------------
   constexpr int ROWS = 16 * MT, COLS = 16 * NT;
   __shared__ float red[WAVES][ROWS][COLS + 1];
+  static_assert(sizeof(red) <= 96 * 1024, "reduction tile too large for this wave count");
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) red[wave][16 * i + 4 * quad + r][16 * s + l16] = yacc[i][s][r];
   __syncthreads();
-  for (int o = threadIdx.x; o < ROWS * COLS; o += 256) {
+  for (int o = threadIdx.x; o < ROWS * COLS; o += 64 * WAVES) {
     const int rr = o / COLS, cc = o % COLS;
     const int m = m0 + rr, n = 16 * s0 + cc;
     if (m < M && n < N) {
@@ -663,6 +663,7 @@ GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size) {
     p.n_tiles = (N / 16 + 15) / 16;
     p.m_tiles = (M + p.mtile - 1) / p.mtile;
     p.nt = 16;
+    p.waves = 4;
     p.workspace_bytes = 0;
     return p;
   }
@@ -673,20 +674,43 @@ GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size) {
   p.n_tiles = (N / 16 + nt - 1) / nt;
   p.m_tiles = (M + p.mtile - 1) / p.mtile;
   p.nt = nt;
+  // Few tiles (small N) leave most CUs idle: 8 waves per workgroup put
+  // twice as much of K in flight, and their partial sums still meet in LDS.
+  // (Measured at M=16, K=14336, N=1024: 4 waves 19.6 us, 8 waves 18.2, 16
+  // waves 21.0; splitting K over workgroups instead, with arrival tickets,
+  // 24-47 us -- its agent-scope fences write back and invalidate the XCD's
+  // L2.)  Every wave keeps >= 2 stages.
+  const long tiles = (long)p.n_tiles * p.m_tiles;
+  const int kb = w_bit == 8 ? 128 : mfma_kblock(w_bit);
+  const int nst = (K + kb - 1) / kb;
+  const bool w8 = nt == 1 && (mt == 1 || (mt == 2 && w_bit != 2));
+  p.waves = (tiles < 128 && w8 && nst >= 16) ? 8 : 4;
+  const int want = env_int("QMM_SKINNY_WAVES");
+  if (want == 4 || (want == 8 && w8)) p.waves = want;
   p.workspace_bytes = 0;
-  (void)K;
   return p;
+}
+
+template <int W_BIT, int XDT, int GS, int MT, int NT, int WAVES>
+static hipError_t launch_skinny_w(const MatmulArgs& a, const GemmPlan& p) {
+  // register budget: 4 waves per SIMD at 16 waves leave 128 registers a lane
+  constexpr int DEPTH = MT >= 4 ? 2 : 3;
+  const long blocks = (long)p.n_tiles * p.m_tiles;
+  hipLaunchKernelGGL((gemm_skinny_kernel<W_BIT, XDT, GS, MT, NT, DEPTH, WAVES>),
+                     dim3((unsigned)blocks), dim3(64 * WAVES), 0, a.stream,
+                     reinterpret_cast<const uint16_t*>(a.x),
+                     reinterpret_cast<const u32x4_t*>(a.Q), a.scales,
+                     reinterpret_cast<const uint32_t*>(a.zeros), a.y, a.M, a.N, a.K, p.n_tiles);
+  return hipGetLastError();
 }
 
 template <int W_BIT, int XDT, int GS, int MT, int NT>
 static hipError_t launch_skinny(const MatmulArgs& a, const GemmPlan& p) {
-  constexpr int DEPTH = MT >= 4 ? 2 : 3;
-  const long blocks = (long)p.n_tiles * p.m_tiles;
-  hipLaunchKernelGGL((gemm_skinny_kernel<W_BIT, XDT, GS, MT, NT, DEPTH>), dim3((unsigned)blocks),
-                     dim3(256), 0, a.stream, reinterpret_cast<const uint16_t*>(a.x),
-                     reinterpret_cast<const u32x4_t*>(a.Q), a.scales,
-                     reinterpret_cast<const uint32_t*>(a.zeros), a.y, a.M, a.N, a.K, p.n_tiles);
-  return hipGetLastError();
+  // 8 waves only where the register ring still fits without spilling
+  if constexpr (NT == 1 && (MT == 1 || (MT == 2 && W_BIT != 2))) {
+    if (p.waves == 8) return launch_skinny_w<W_BIT, XDT, GS, MT, NT, 8>(a, p);
+  }
+  return launch_skinny_w<W_BIT, XDT, GS, MT, NT, 4>(a, p);
 }
 
 template <int W_BIT, int XDT, int GS, int MT>

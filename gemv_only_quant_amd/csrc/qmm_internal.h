@@ -51,6 +51,7 @@ struct GemmPlan {
   int kind;      // 0: skinny (registers-direct, K split over the waves), 1: large-M tiled
   int mtile;     // rows per M tile
   int nt;        // 16-column strips per workgroup (skinny)
+  int waves;     // waves per workgroup, splitting K (skinny: 4 or 8)
   int n_tiles;
   int m_tiles;
   size_t workspace_bytes;  // always 0 in this version: no kernel needs one

@@ -138,6 +138,8 @@ def workload(name):
             return int8_case(M, 14336, 4096, BF16, seed=3000 + M, name=name)
     if name == "int4_g128_sym_m16_k8192_n8192":
         return lowbit_case(16, 8192, 8192, 4, 128, F16, True, seed=4000, x_std=0.5, name=name)
+    if name == "int4_g128_asym_smalln_m16_k14336_n1024":
+        return lowbit_case(16, 1024, 14336, 4, 128, BF16, False, seed=6000, name=name)
     if name == "int4_g128_asym_prefill_m4096_k4096_n11008":
         return lowbit_case(4096, 11008, 4096, 4, 128, BF16, False, seed=5004, name=name)
     if name == "int2_g64_asym_prefill_m4096_k4096_n11008":
@@ -152,6 +154,7 @@ WORKLOADS = [
     "int8_skinny_m32_k4096_n14336",
     "int8_skinny_m64_k4096_n14336",
     "int4_g128_sym_m16_k8192_n8192",
+    "int4_g128_asym_smalln_m16_k14336_n1024",
     "int4_g128_asym_prefill_m4096_k4096_n11008",
     "int2_g64_asym_prefill_m4096_k4096_n11008",
 ]

@@ -117,6 +117,7 @@ def test_workspace_reused_across_calls():
 
 FULL = ["int8_skinny_m16_k4096_n14336", "int8_skinny_m32_k4096_n14336",
         "int8_skinny_m64_k4096_n14336", "int4_g128_sym_m16_k8192_n8192",
+        "int4_g128_asym_smalln_m16_k14336_n1024",
         "int4_g128_asym_prefill_m4096_k4096_n11008", "int2_g64_asym_prefill_m4096_k4096_n11008"]
 
 
@@ -175,3 +176,44 @@ def test_gemm_large_one_hot_reproduces_weights():
     W = oracle.dequant(case.np_Q(), case.np_scales(), case.np_zeros(), N, K, 4, 128)
     for m, k in enumerate(ks):
         assert np.array_equal(y[m], W[k]), (m, k)
+
+
+# ------------------------------------ small N, long K: 8 waves split K per tile
+MANYWAVES = [  # M, N, K, w_bit, group, x_dtype, symmetric, forced waves (0 = planner's)
+    (16, 64, 4096, 4, 128, si.F16, False, 0),      # 4 tiles, 32 stages -> 8 waves
+    (3, 256, 8192, 4, 64, si.BF16, False, 0),      # ragged M
+    (1, 32, 6144, 4, 256, si.F16, True, 0),        # 48 stages: uneven shares
+    (16, 80, 5120, 4, 32, si.BF16, False, 8),      # 40 stages over 8 waves, g32
+    (30, 48, 4096, 4, 128, si.F16, False, 0),      # two 16-row tiles -> 8 waves
+    (16, 48, 8192, 2, 64, si.BF16, False, 0),      # int2 -> 8 waves
+    (9, 16, 1152, 4, 128, si.BF16, False, 8),      # 9 stages: waves 5..7 idle
+]
+
+
+@pytest.mark.parametrize("M,N,K,w_bit,gs,xdt,sym,waves", MANYWAVES)
+def test_gemm_many_waves_within_bound(M, N, K, w_bit, gs, xdt, sym, waves, monkeypatch):
+    if waves:
+        monkeypatch.setenv("QMM_SKINNY_WAVES", str(waves))
+    case = si.lowbit_case(M, N, K, w_bit, gs, xdt, sym, seed=900 + M + N + K)
+    y = run_gemm(case)
+    y_ref, a_ref = oracle.qmm(*case.oracle_args())
+    assert_within_bound(y, y_ref, a_ref, f"waves w{w_bit} M{M} N{N} K{K}")
+
+
+@pytest.mark.parametrize("M,N,K,xdt", [(16, 64, 8192, si.BF16), (7, 32, 4096, si.F16)])
+def test_gemm_many_waves_int8_within_bound(M, N, K, xdt):
+    case = si.int8_case(M, N, K, xdt, seed=950 + M + K)
+    y = run_gemm(case)
+    y_ref, a_ref = oracle.qmm(*case.oracle_args())
+    assert_within_bound(y, y_ref, a_ref, f"waves int8 M{M} N{N} K{K}")
+
+
+@pytest.mark.parametrize("M,N,K,w_bit,gs,waves", [(16, 64, 4096, 4, 128, 8),
+                                                  (5, 32, 8192, 2, 64, 8),
+                                                  (20, 16, 4096, 4, 64, 8)])
+def test_gemm_many_waves_exact_probe_bit_exact(M, N, K, w_bit, gs, waves, monkeypatch):
+    monkeypatch.setenv("QMM_SKINNY_WAVES", str(waves))
+    case = si.exact_lowbit_case(M, N, K, w_bit, gs, si.BF16, False, seed=M + N)
+    y = run_gemm(case)
+    y_ref, _ = oracle.qmm(*case.oracle_args())
+    assert np.array_equal(y.astype(np.float64), y_ref)
