@@ -38,45 +38,53 @@ POOL_BYTES = 512 << 20          # weight pool for memory-bound workloads
 HEADLINE = "int4_g128_asym_gemv_m1_k4096_n4096"
 OTHERS = [  # (workload, entry)
     ("int8_gemv_m1_k1024_n1024", "gemv"),
+    ("int4_pc_sym_gemv_m1_k4096_n4096", "gemv"),  # per-column scales
     ("int8_skinny_m16_k4096_n14336", "gemm"),
     ("int8_skinny_m32_k4096_n14336", "gemm"),
     ("int8_skinny_m64_k4096_n14336", "gemm"),
     ("int4_g128_sym_m16_k8192_n8192", "gemm"),
     ("int4_g128_asym_smalln_m16_k14336_n1024", "gemm"),  # 64 tiles: 8 waves each
 ]
-PREFILL = ["int4_g128_asym_prefill_m4096_k4096_n11008",
-           "int2_g64_asym_prefill_m4096_k4096_n11008"]
+PREFILL = [  # (workload, output dtype)
+    ("int4_g128_asym_prefill_m4096_k4096_n11008", "f32"),
+    ("int2_g64_asym_prefill_m4096_k4096_n11008", "f32"),
+    ("int4_g128_asym_prefill_m4096_k4096_n11008", "bf16"),  # qmm_gemm_ex, bf16 y
+]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 CSRC = os.path.join(ROOT, "gemv_only_quant_amd", "csrc")
 
 
-def bytes_of(case):
+def bytes_of(case, y_bytes=4):
     """Algorithmic bytes per call: packed Q, scales, zeros, x and y, each once."""
     w = case.Q.numel() * case.Q.element_size()
     w += case.scales.numel() * case.scales.element_size()
     if case.zeros is not None:
         w += case.zeros.numel() * case.zeros.element_size()
-    io = case.x.numel() * case.x.element_size() + case.M * case.N * 4
+    io = case.x.numel() * case.x.element_size() + case.M * case.N * y_bytes
     return w, w + io
 
 
-def time_workload(name, steps, warmup, path):
+def time_workload(name, steps, warmup, path, out="f32"):
     """Average µs per call of `steps` graph-replayed calls (plus eager µs)."""
     import torch
     import gemv_only_quant_amd as qmm
     import synth_inputs as si
 
+    ydt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[out]
     case = si.workload(name)
-    wbytes, tbytes = bytes_of(case)
+    wbytes, tbytes = bytes_of(case, torch.tensor([], dtype=ydt).element_size())
     d = case.to("cuda")
     Q0 = d.Q if path == "gemv" else qmm.pack(d.Q, case.N, case.K, case.w_bit)
     copies = 1 if case.M >= 1024 else max(1, -(-POOL_BYTES // wbytes))
     pool = [(Q0, d.scales, d.zeros)]
     for _ in range(copies - 1):
         pool.append((Q0.clone(), d.scales.clone(), None if d.zeros is None else d.zeros.clone()))
-    y = torch.empty((case.M, case.N), dtype=torch.float32, device="cuda")
+    y = torch.empty((case.M, case.N), dtype=ydt, device="cuda")
     ws = qmm.workspace_for(case.M, case.N, case.K, case.w_bit, case.group_size, "cuda")
-    fn = qmm.qmm_gemv if path == "gemv" else qmm.qmm_gemm
+    if out == "f32":
+        fn = qmm.qmm_gemv if path == "gemv" else qmm.qmm_gemm
+    else:
+        fn = qmm.qmm_gemv_ex if path == "gemv" else qmm.qmm_gemm_ex
 
     def call(i):
         Q, s, z = pool[i % copies]
@@ -263,10 +271,11 @@ def main():
     if not args.quick:
         out["workloads"] = [line(time_workload(n, 200, 20, p), p) for n, p in OTHERS]
         pre = []
-        for n in PREFILL:
-            p = time_workload(n, 10, 3, "gemm")
+        for n, out_dt in PREFILL:
+            p = time_workload(n, 10, 3, "gemm", out_dt)
             tf = p["flops"] / (p["us"] * 1e-6) / 1e12
-            pre.append({"workload": n, "entry": "qmm_gemm", "us_per_call": round(p["us"], 2),
+            pre.append({"workload": n, "entry": "qmm_gemm" if out_dt == "f32" else "qmm_gemm_ex",
+                        "y_dtype": out_dt, "us_per_call": round(p["us"], 2),
                         "tflops": round(tf, 2), "peak_tflops": MFMA_PEAK_TFLOPS,
                         "frac": round(tf / MFMA_PEAK_TFLOPS, 4)})
         out["prefill"] = pre

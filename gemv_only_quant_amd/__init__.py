@@ -17,7 +17,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqmm.so")
 
 QMM_OK, QMM_ERR_ARG, QMM_ERR_UNSUPPORTED, QMM_ERR_DEVICE = 0, 1, 2, 3
-QMM_F16, QMM_BF16 = 0, 1
+QMM_F16, QMM_BF16, QMM_F32 = 0, 1, 2
+QMM_PER_COLUMN = -1  # group_size for per-column scales (one group spanning K)
 QMM_LAYOUT_CANON, QMM_LAYOUT_MFMA = 0, 1
 
 if not os.path.exists(LIB_PATH):
@@ -34,14 +35,19 @@ _lib.qmm_unpack_layout.argtypes = [_P, _P, _I, _I, _I, _P]
 _lib.qmm_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
 _lib.qmm_workspace_bytes.restype = _S
 _MATMUL = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _S, _P]
+_MATMUL_EX = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _S, _P]
 _lib.qmm_gemv.argtypes = _MATMUL
 _lib.qmm_gemm.argtypes = _MATMUL
+_lib.qmm_gemv_ex.argtypes = _MATMUL_EX
+_lib.qmm_gemm_ex.argtypes = _MATMUL_EX
 _lib.qmm_dequant.argtypes = [_P, _I, _P, _P, _P, _I, _I, _I, _I, _P]
-for _f in ("qmm_pack", "qmm_unpack_layout", "qmm_gemv", "qmm_gemm", "qmm_dequant"):
+for _f in ("qmm_pack", "qmm_unpack_layout", "qmm_gemv", "qmm_gemm", "qmm_gemv_ex", "qmm_gemm_ex",
+           "qmm_dequant"):
     getattr(_lib, _f).restype = _I
 
 EXPORTS = ("qmm_version", "qmm_last_error", "qmm_packed_bytes", "qmm_pack",
-           "qmm_unpack_layout", "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm", "qmm_dequant")
+           "qmm_unpack_layout", "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm", "qmm_gemv_ex",
+           "qmm_gemm_ex", "qmm_dequant")
 
 
 class QmmError(ValueError):
@@ -128,6 +134,39 @@ def qmm_gemm(x, Q, scales, zeros, y, M, N, K, w_bit, group_size, x_dtype=None,
             workspace, workspace_bytes, stream)
 
 
+def _y_code(y):
+    if isinstance(y, torch.Tensor):
+        codes = {torch.float32: QMM_F32, torch.float16: QMM_F16, torch.bfloat16: QMM_BF16}
+        if y.dtype not in codes:
+            raise QmmError(QMM_ERR_ARG, f"y must be float32, float16 or bfloat16, got {y.dtype}")
+        return codes[y.dtype]
+    raise QmmError(QMM_ERR_ARG, "y_dtype must be given when y is a raw pointer")
+
+
+def _matmul_ex(fn, x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit, group_size, x_dtype,
+               workspace, workspace_bytes, stream):
+    if x_dtype is None:
+        x_dtype = _dtype_code(x)
+    if y_dtype is None:
+        y_dtype = _y_code(y)
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(fn(_ptr(x), _ptr(Q), _ptr(scales), _ptr(zeros), _ptr(y), y_dtype, M, N, K, w_bit,
+              group_size, x_dtype, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def qmm_gemv_ex(x, Q, scales, zeros, y, M, N, K, w_bit, group_size, y_dtype=None, x_dtype=None,
+                workspace=None, workspace_bytes=None, stream=None):
+    _matmul_ex(_lib.qmm_gemv_ex, x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit, group_size,
+               x_dtype, workspace, workspace_bytes, stream)
+
+
+def qmm_gemm_ex(x, Q, scales, zeros, y, M, N, K, w_bit, group_size, y_dtype=None, x_dtype=None,
+                workspace=None, workspace_bytes=None, stream=None):
+    _matmul_ex(_lib.qmm_gemm_ex, x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit, group_size,
+               x_dtype, workspace, workspace_bytes, stream)
+
+
 def qmm_dequant(Q, layout, scales, zeros, w_out, N, K, w_bit, group_size, stream=None):
     _check(_lib.qmm_dequant(_ptr(Q), layout, _ptr(scales), _ptr(zeros), _ptr(w_out), N, K,
                             w_bit, group_size, _stream(stream)))
@@ -162,12 +201,13 @@ def _dims(x, Q, w_bit, canonical):
     return M, N, K
 
 
-def gemv(x, Q, scales, zeros, w_bit, group_size, out=None):
-    """y = x @ dequant(Q) for 1 <= M <= 16, Q in the canonical layout."""
+def gemv(x, Q, scales, zeros, w_bit, group_size, out=None, out_dtype=torch.float32):
+    """y = x @ dequant(Q) for 1 <= M <= 16, Q in the canonical layout; y is
+    `out`, else a new (M, N) tensor of out_dtype (float32, float16, bfloat16)."""
     M, N, K = _dims(x, Q, w_bit, True)
-    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=x.device)
+    y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=x.device)
     ws = workspace_for(M, N, K, w_bit, group_size, x.device)
-    qmm_gemv(x, Q, scales, zeros, y, M, N, K, w_bit, group_size, workspace=ws)
+    qmm_gemv_ex(x, Q, scales, zeros, y, M, N, K, w_bit, group_size, workspace=ws)
     return y
 
 
@@ -179,12 +219,12 @@ def pack(Q, N, K, w_bit):
     return out
 
 
-def gemm(x, Q_mfma, scales, zeros, N, w_bit, group_size, out=None):
-    """y = x @ dequant(Q) for any M >= 1, Q in the MFMA layout."""
+def gemm(x, Q_mfma, scales, zeros, N, w_bit, group_size, out=None, out_dtype=torch.float32):
+    """y = x @ dequant(Q) for any M >= 1, Q in the MFMA layout; y as in gemv."""
     M, K = x.shape
-    y = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=x.device)
+    y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=x.device)
     ws = workspace_for(M, N, K, w_bit, group_size, x.device)
-    qmm_gemm(x, Q_mfma, scales, zeros, y, M, N, K, w_bit, group_size, workspace=ws)
+    qmm_gemm_ex(x, Q_mfma, scales, zeros, y, M, N, K, w_bit, group_size, workspace=ws)
     return y
 
 

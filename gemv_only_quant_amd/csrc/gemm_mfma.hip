@@ -18,6 +18,8 @@
 //        y += s * (acc - (B + z) * xsum)
 //    in fp32 -- so the matrix cores only see exact integers and the group
 //    scale is applied once per group (the page's w = (q - z) * s, regrouped).
+#include <type_traits>
+
 #include "qmm_device.h"
 #include "qmm_internal.h"
 
@@ -87,8 +89,9 @@ __device__ __forceinline__ u32x4_t bfrag(const u32x4_t* slot, int st) {
 template <int W_BIT, int XDT, int GS, int MT, int NT, int DEPTH, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ Qt,
-    const void* __restrict__ scales, const uint32_t* __restrict__ qz, float* __restrict__ y,
-    int M, int N, int K, int n_tiles) {
+    const void* __restrict__ scales, const uint32_t* __restrict__ qz, void* __restrict__ y,
+    int M, int N, int K, int tile_opts) {
+  const int n_tiles = tiles_of(tile_opts), ydt = ydt_of(tile_opts), gmask = gmask_of(tile_opts);
   constexpr int KB = Stage<W_BIT>::KB;
   constexpr int BLK = Stage<W_BIT>::BLK;
   constexpr int KS = KB * BLK;           // k per stage
@@ -155,8 +158,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
       for (int s = 0; s < NT; ++s) {
         const int n = 16 * sidx[s] + l16;
 #pragma unroll
-        for (int q = 0; q < NGS; ++q) R.sc[s][q] = s16[(size_t)(g0 + q) * N + n];
-        R.zw[s] = qz != nullptr ? qz[(size_t)(g0 / PACK) * N + n] : ZSYM;
+        for (int q = 0; q < NGS; ++q) R.sc[s][q] = s16[(size_t)((g0 + q) & gmask) * N + n];
+        R.zw[s] = qz != nullptr ? qz[(size_t)((g0 & gmask) / PACK) * N + n] : ZSYM;
       }
     }
   };
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
         const int kend = st * KS + 32 * (k + 1);  // one past this step
         if (kend % GS == 0 || (k == STEPS - 1 && last)) {
           const int q = GS < KS ? (32 * k) / GS : 0;
-          const int g = (st * KS) / GS + q;
+          const int g = ((st * KS) / GS + q) & gmask;
           float sc[NT], bz[NT];
 #pragma unroll
           for (int s = 0; s < NT; ++s) {
@@ -251,16 +254,19 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) red[wave][16 * i + 4 * quad + r][16 * s + l16] = yacc[i][s][r];
   __syncthreads();
-  for (int o = threadIdx.x; o < ROWS * COLS; o += 64 * WAVES) {
-    const int rr = o / COLS, cc = o % COLS;
-    const int m = m0 + rr, n = 16 * s0 + cc;
-    if (m < M && n < N) {
-      float sum = 0.f;
+  with_y(y, ydt, [&](auto* yt) {
+    using T = typename std::remove_pointer<decltype(yt)>::type;
+    for (int o = threadIdx.x; o < ROWS * COLS; o += 64 * WAVES) {
+      const int rr = o / COLS, cc = o % COLS;
+      const int m = m0 + rr, n = 16 * s0 + cc;
+      if (m < M && n < N) {
+        float sum = 0.f;
 #pragma unroll
-      for (int v = 0; v < WAVES; ++v) sum += red[v][rr][cc];
-      y[(size_t)m * N + n] = sum;
+        for (int v = 0; v < WAVES; ++v) sum += red[v][rr][cc];
+        yt[(size_t)m * N + n] = (T)sum;
+      }
     }
-  }
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -387,8 +393,9 @@ __device__ __forceinline__ uint32_t bpair_scaled(uint32_t w, int h, int t, const
 template <int W_BIT, int XDT, int GS, bool ZP, int MT>
 __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ Qt,
-    const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qz, float* __restrict__ y,
-    int M, int N, int K, int n_tiles) {
+    const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qz, void* __restrict__ y,
+    int M, int N, int K, int tile_opts) {
+  const int n_tiles = tiles_of(tile_opts), ydt = ydt_of(tile_opts), gmask = gmask_of(tile_opts);
   constexpr int BM = 16 * MT;          // rows per workgroup (MT 16-row tiles)
   constexpr int NT = 4;                 // strips per wave
   constexpr int KS = 128;               // k per stage
@@ -451,8 +458,8 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
       R.slot[s] = Qt[((size_t)sidx[s] * nblk + kb) * 64 + lane];
       const int n = 16 * sidx[s] + l16;
 #pragma unroll
-      for (int q = 0; q < NGS; ++q) R.sc[s][q] = scales[(size_t)(g0 + q) * N + n];
-      if constexpr (ZP) R.zw[s] = qz[(size_t)(g0 / PACK) * N + n];
+      for (int q = 0; q < NGS; ++q) R.sc[s][q] = scales[(size_t)((g0 + q) & gmask) * N + n];
+      if constexpr (ZP) R.zw[s] = qz[(size_t)((g0 & gmask) / PACK) * N + n];
       else R.zw[s] = ZSYM;
     }
   };
@@ -470,10 +477,10 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
       R.slot[j] = Qt[((size_t)sidx[j] * nblk + kb) * 64 + lane];
     } else if (j < NT + NT * NGS) {
       const int s = (j - NT) / NGS, q = (j - NT) % NGS;
-      R.sc[s][q] = scales[(size_t)(g0 + q) * N + 16 * sidx[s] + l16];
+      R.sc[s][q] = scales[(size_t)((g0 + q) & gmask) * N + 16 * sidx[s] + l16];
     } else if (j < NWL) {
       const int s = j - NT - NT * NGS;
-      if constexpr (ZP) R.zw[s] = qz[(size_t)(g0 / PACK) * N + 16 * sidx[s] + l16];
+      if constexpr (ZP) R.zw[s] = qz[(size_t)((g0 & gmask) / PACK) * N + 16 * sidx[s] + l16];
       else R.zw[s] = ZSYM;
     } else {
       const int f = wave * (FRAGS / 4) + (j - NWL);
@@ -499,7 +506,7 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
     for (int q = 0; q < NGS; ++q) {
       const uint32_t sb = R.sc[s][q] & 0xFFFFu;
       const float sc = f16_bits_to_f32((uint16_t)sb);
-      const uint32_t z = (R.zw[s] >> (((g0 + q) % PACK) * W_BIT)) & ((1u << W_BIT) - 1u);
+      const uint32_t z = (R.zw[s] >> ((((g0 + q) & gmask) % PACK) * W_BIT)) & ((1u << W_BIT) - 1u);
       const float zb = 1024.0f + (float)z;
       g[q].s = sc;
       g[q].zb_s = zb * sc;
@@ -623,23 +630,33 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
     __syncthreads();
   }
   // the accumulators were last written by MFMAs the compiler does not see
-  // as such: give them their result latency before they are read
+  // as such: give them their result latency before they are read.  Each
+  // accumulator then passes through an empty asm ordered after the wait, so
+  // no read of it can be moved above the wait (they are register reads,
+  // which the wait's memory clobber alone does not hold back).
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int s = 0; s < NT; ++s) asm volatile("" : "+a"(acc[i][s]));
   __builtin_amdgcn_sched_barrier(0);
 
+  with_y(y, ydt, [&](auto* yt) {
+    using T = typename std::remove_pointer<decltype(yt)>::type;
 #pragma unroll
-  for (int s = 0; s < NT; ++s) {
-    if (s0 + s >= strips) continue;
-    const int n = 16 * (s0 + s) + l16;
+    for (int s = 0; s < NT; ++s) {
+      if (s0 + s >= strips) continue;
+      const int n = 16 * (s0 + s) + l16;
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+      for (int i = 0; i < MT; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 16 * i + 4 * quad + r;
-        if (m < M) y[(size_t)m * N + n] = acc[i][s][r];
-      }
-  }
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + 16 * i + 4 * quad + r;
+          if (m < M) yt[(size_t)m * N + n] = (T)acc[i][s][r];
+        }
+    }
+  });
 }
 
 // ---------------------------------------------------------------- host side
@@ -700,7 +717,8 @@ static hipError_t launch_skinny_w(const MatmulArgs& a, const GemmPlan& p) {
                      dim3((unsigned)blocks), dim3(64 * WAVES), 0, a.stream,
                      reinterpret_cast<const uint16_t*>(a.x),
                      reinterpret_cast<const u32x4_t*>(a.Q), a.scales,
-                     reinterpret_cast<const uint32_t*>(a.zeros), a.y, a.M, a.N, a.K, p.n_tiles);
+                     reinterpret_cast<const uint32_t*>(a.zeros), a.y,
+                     a.M, a.N, a.K, pack_tiles(p.n_tiles, a.y_dtype, a.group_mask == 0));
   return hipGetLastError();
 }
 
@@ -754,7 +772,8 @@ static hipError_t launch_large_mt(const MatmulArgs& a, const GemmPlan& p) {
                      dim3(256), 0, a.stream, reinterpret_cast<const uint16_t*>(a.x),
                      reinterpret_cast<const u32x4_t*>(a.Q),
                      reinterpret_cast<const uint16_t*>(a.scales),
-                     reinterpret_cast<const uint32_t*>(a.zeros), a.y, a.M, a.N, a.K, p.n_tiles);
+                     reinterpret_cast<const uint32_t*>(a.zeros), a.y,
+                     a.M, a.N, a.K, pack_tiles(p.n_tiles, a.y_dtype, a.group_mask == 0));
   return hipGetLastError();
 }
 

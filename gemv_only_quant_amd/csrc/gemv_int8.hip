@@ -14,6 +14,8 @@
 //                                                           bias C = 128
 // and the bias leaves once per lane: sum x (C + q) - C sum x.  The 64 lane
 // partials of each (m, n) are folded with DPP (qmm_device.h wave_sum).
+#include <type_traits>
+
 #include "qmm_device.h"
 #include "qmm_internal.h"
 
@@ -48,7 +50,7 @@ template <> struct Int8Pairs<XBF16> {
 template <int XDT, int MB, int RN>
 __global__ __launch_bounds__(256) void gemv_int8_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ Q,
-    const float* __restrict__ scale, float* __restrict__ y, int M, int N, int K) {
+    const float* __restrict__ scale, void* __restrict__ y, int ydt, int M, int N, int K) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int n0 = (blockIdx.x * 4 + wave) * RN;
@@ -93,15 +95,20 @@ __global__ __launch_bounds__(256) void gemv_int8_kernel(
     }
   }
 
+  float v[MB][RN];
 #pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    if (m < M) {
+  for (int m = 0; m < MB; ++m)
 #pragma unroll
-      for (int r = 0; r < RN; ++r) {
-        const float v = wave_sum(acc[m][r] - Int8Pairs<XDT>::bias * xs[m]);
-        if (lane == 0 && n0 + r < N) y[(size_t)m * N + n0 + r] = scale[n0 + r] * v;
-      }
-    }
+    for (int r = 0; r < RN; ++r) v[m][r] = m < M ? wave_sum(acc[m][r] - Int8Pairs<XDT>::bias * xs[m]) : 0.f;
+  if (lane == 0) {
+    with_y(y, ydt, [&](auto* yt) {
+      using T = typename std::remove_pointer<decltype(yt)>::type;
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int r = 0; r < RN; ++r)
+          if (m < M && n0 + r < N) yt[(size_t)m * N + n0 + r] = (T)(scale[n0 + r] * v[m][r]);
+    });
   }
 }
 
@@ -129,9 +136,9 @@ static hipError_t launch8(const MatmulArgs& a, const GemvInt8Plan& p) {
   auto Q = reinterpret_cast<const int8_t*>(a.Q);
   auto s = reinterpret_cast<const float*>(a.scales);
   switch (p.rn) {
-    case 1: hipLaunchKernelGGL((gemv_int8_kernel<XDT, MB, 1>), grid, block, 0, a.stream, xq, Q, s, a.y, a.M, a.N, a.K); break;
-    case 2: hipLaunchKernelGGL((gemv_int8_kernel<XDT, MB, 2>), grid, block, 0, a.stream, xq, Q, s, a.y, a.M, a.N, a.K); break;
-    case 4: hipLaunchKernelGGL((gemv_int8_kernel<XDT, MB, 4>), grid, block, 0, a.stream, xq, Q, s, a.y, a.M, a.N, a.K); break;
+    case 1: hipLaunchKernelGGL((gemv_int8_kernel<XDT, MB, 1>), grid, block, 0, a.stream, xq, Q, s, a.y, a.y_dtype, a.M, a.N, a.K); break;
+    case 2: hipLaunchKernelGGL((gemv_int8_kernel<XDT, MB, 2>), grid, block, 0, a.stream, xq, Q, s, a.y, a.y_dtype, a.M, a.N, a.K); break;
+    case 4: hipLaunchKernelGGL((gemv_int8_kernel<XDT, MB, 4>), grid, block, 0, a.stream, xq, Q, s, a.y, a.y_dtype, a.M, a.N, a.K); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

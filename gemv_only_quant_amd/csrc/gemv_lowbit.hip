@@ -24,16 +24,23 @@
 //    and the group scale multiplies that once: r += s * (...);
 //  * the 16 row-lanes of a wave that share a column quad are summed with
 //    cross-lane shuffles, then the 4 waves through LDS.
+#include <type_traits>
+
 #include "qmm_device.h"
 #include "qmm_internal.h"
 
 namespace qmm {
 
-template <int W_BIT, int XDT, int MB, int RL, int CQ, int WAVES>
+// Y32: fp32 output; else fp16 / bf16, the type in bits 8+ of m_ydt (M <= 16
+// in bits 0-7: the output type rides on M so that the explicit arguments
+// stay within 56 bytes, see pack_tiles).
+template <int W_BIT, int XDT, int MB, int RL, int CQ, int WAVES, bool Y32>
 __global__ __launch_bounds__(64 * WAVES) void gemv_lowbit_kernel(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
-    const uint16_t* __restrict__ sc, const uint32_t* __restrict__ qz, float* __restrict__ y,
-    int M, int N, int K, int group_size) {
+    const uint16_t* __restrict__ sc, const uint32_t* __restrict__ qz, void* __restrict__ y,
+    int m_ydt, int N, int K, int group_size) {
+  const int M = Y32 ? m_ydt : (m_ydt & 0xFF);
+  const int ydt = Y32 ? (int)YF32 : (m_ydt >> 8);
   constexpr int PACK = 32 / W_BIT;   // codes per word
   constexpr int PAIRS = PACK / 2;    // 16-bit pairs per word
   constexpr uint32_t FIELD2 = W_BIT == 4 ? 0x000F000Fu : 0x00030003u;
@@ -194,16 +201,21 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lowbit_kernel(
       for (int c = 0; c < 4; ++c) red[(wave * MB + m) * CW + cq * 4 + c] = r[m][c];
   }
   __syncthreads();
-  for (int o = threadIdx.x; o < MB * CW; o += NT) {
-    const int m = o / CW, col = o % CW;
-    const int n = tile * CW + col;
-    if (m < M && n < N) {
-      float sum = 0.f;
+  auto store = [&](auto* yt) {
+    using T = typename std::remove_pointer<decltype(yt)>::type;
+    for (int o = threadIdx.x; o < MB * CW; o += NT) {
+      const int m = o / CW, col = o % CW;
+      const int n = tile * CW + col;
+      if (m < M && n < N) {
+        float sum = 0.f;
 #pragma unroll
-      for (int v = 0; v < WAVES; ++v) sum += red[(v * MB + m) * CW + col];
-      y[(size_t)m * N + n] = sum;
+        for (int v = 0; v < WAVES; ++v) sum += red[(v * MB + m) * CW + col];
+        yt[(size_t)m * N + n] = (T)sum;
+      }
     }
-  }
+  };
+  if constexpr (Y32) store(reinterpret_cast<float*>(y));
+  else with_y(y, ydt, store);
 }
 
 // ---------------------------------------------------------------- host side
@@ -221,12 +233,14 @@ GemvLowbitPlan plan_gemv_lowbit(int M, int N, int K, int w_bit, int group_size) 
   const int pack = 32 / w_bit;
   const int pairs = pack / 2;
   const int rows = K / pack;
-  const int rpg = group_size / pack;  // packed rows per group (power of two)
+  const int rpg = group_size / pack;  // packed rows per group
   p.mb = m_bucket(M);
   p.n_tiles = (N + 15) / 16;
   // rows per lane: a power of two dividing the group, no more than the 64
   // row-lanes need to cover K in one pass, and an x slice within 64 KiB
-  int rl = rpg < 16 ? rpg : 16;
+  // (per-column scales: the group is all of K, rpg = K / pack, an even number)
+  int rl = 16;
+  while (rl > 2 && (rl > rpg || rpg % rl != 0)) rl /= 2;
   while (rl > 2 && rl * 64 / 2 >= rows) rl /= 2;
   while (rl > 2 && x_lds_bytes(p.mb, rl, pairs) > kXldsMax) rl /= 2;
   const int want = env_int("QMM_GEMV_RL");
@@ -241,12 +255,13 @@ static hipError_t launch_rl(const MatmulArgs& a, const GemvLowbitPlan& p) {
   if constexpr (x_lds_bytes(MB, RL, 16 / W_BIT) > kXldsMax && RL > 2) {
     return hipErrorInvalidValue;  // never planned
   } else {
-  hipLaunchKernelGGL((gemv_lowbit_kernel<W_BIT, XDT, MB, RL, 4, 4>), dim3(p.n_tiles), dim3(256), 0,
-                     a.stream, reinterpret_cast<const uint16_t*>(a.x),
-                     reinterpret_cast<const uint32_t*>(a.Q),
+  const auto k = a.y_dtype == YF32 ? gemv_lowbit_kernel<W_BIT, XDT, MB, RL, 4, 4, true>
+                                   : gemv_lowbit_kernel<W_BIT, XDT, MB, RL, 4, 4, false>;
+  hipLaunchKernelGGL(k, dim3(p.n_tiles), dim3(256), 0, a.stream,
+                     reinterpret_cast<const uint16_t*>(a.x), reinterpret_cast<const uint32_t*>(a.Q),
                      reinterpret_cast<const uint16_t*>(a.scales),
-                     reinterpret_cast<const uint32_t*>(a.zeros), a.y, a.M, a.N, a.K,
-                     a.group_size);
+                     reinterpret_cast<const uint32_t*>(a.zeros), a.y,
+                     a.y_dtype == YF32 ? a.M : (a.M | (a.y_dtype << 8)), a.N, a.K, a.group_size);
   return hipGetLastError();
   }
 }

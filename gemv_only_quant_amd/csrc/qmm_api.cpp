@@ -44,9 +44,15 @@ qmm_status check_operands(const char* fn, const void* Q, const void* scales, con
       return fail(QMM_ERR_ARG, "%s: int8 uses a per-row scale; group_size must be 0 (got %d)",
                   fn, group_size);
     if (zeros != nullptr) return fail(QMM_ERR_ARG, "%s: int8 takes no zero points", fn);
+  } else if (group_size == QMM_PER_COLUMN) {
+    if (K % (32 / w_bit) != 0)
+      return fail(QMM_ERR_ARG, "%s: K=%d is not a multiple of %d", fn, K, 32 / w_bit);
+    if (K % 32 != 0)
+      return fail(QMM_ERR_UNSUPPORTED, "%s: per-column scales need K %% 32 == 0 (K=%d)", fn, K);
   } else {
     if (group_size <= 0)
-      return fail(QMM_ERR_ARG, "%s: group_size must be positive (got %d)", fn, group_size);
+      return fail(QMM_ERR_ARG, "%s: group_size must be positive or QMM_PER_COLUMN (got %d)", fn,
+                  group_size);
     if (K % group_size != 0)
       return fail(QMM_ERR_ARG, "%s: K=%d is not a multiple of group_size=%d", fn, K, group_size);
     if (!group_supported(group_size))
@@ -65,11 +71,14 @@ qmm_status check_operands(const char* fn, const void* Q, const void* scales, con
 }
 
 qmm_status check_matmul(const char* fn, const void* x, const void* Q, const void* scales,
-                        const void* zeros, const float* y, int M, int N, int K, int w_bit,
-                        int group_size, int x_dtype, bool* noop) {
+                        const void* zeros, const void* y, int y_dtype, int M, int N, int K,
+                        int w_bit, int group_size, int x_dtype, bool* noop) {
   if (M < 0) return fail(QMM_ERR_ARG, "%s: negative M=%d", fn, M);
   if (x_dtype != QMM_F16 && x_dtype != QMM_BF16)
     return fail(QMM_ERR_ARG, "%s: x_dtype must be QMM_F16 or QMM_BF16 (got %d)", fn, x_dtype);
+  if (y_dtype != QMM_F32 && y_dtype != QMM_F16 && y_dtype != QMM_BF16)
+    return fail(QMM_ERR_ARG, "%s: y_dtype must be QMM_F32, QMM_F16 or QMM_BF16 (got %d)", fn,
+                y_dtype);
   qmm_status st = check_operands(fn, Q, scales, zeros, N, K, w_bit, group_size, noop);
   if (st != QMM_OK || *noop) return st;
   if (M == 0) {
@@ -104,6 +113,17 @@ bool gemv_shape_ok(int N, int K, int w_bit) {
 bool gemm_shape_ok(int N, int K, int w_bit) {
   return N % 16 == 0 && K % qmm::mfma_kblock(w_bit) == 0;
 }
+
+// Per-column scales are one group spanning K.  The GEMV and dequant kernels
+// take the group size at run time, so there it is K itself; the GEMM
+// kernels are built for fixed group sizes, so they run the largest built
+// size dividing K with every group index masked to 0.
+int gemv_group(int K, int group_size) { return group_size == QMM_PER_COLUMN ? K : group_size; }
+int gemm_group(int K, int group_size) {
+  if (group_size != QMM_PER_COLUMN) return group_size;
+  return K % 256 == 0 ? 256 : (K % 128 == 0 ? 128 : (K % 64 == 0 ? 64 : 32));
+}
+int group_mask(int group_size) { return group_size == QMM_PER_COLUMN ? 0 : -1; }
 
 }  // namespace
 
@@ -167,27 +187,33 @@ qmm_status qmm_unpack_layout(const void* Q_mfma, void* Q_canon, int N, int K, in
 size_t qmm_workspace_bytes(int M, int N, int K, int w_bit, int group_size) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
   if (w_bit != 2 && w_bit != 4 && w_bit != 8) return 0;
-  if (w_bit != 8 && (group_size <= 0 || K % group_size != 0 || !group_supported(group_size)))
-    return 0;
+  if (w_bit != 8) {
+    if (group_size == QMM_PER_COLUMN) {
+      if (K % 32 != 0) return 0;
+    } else if (group_size <= 0 || K % group_size != 0 || !group_supported(group_size)) {
+      return 0;
+    }
+  }
   size_t need = 0;
   if (M <= 16 && w_bit != 8 && gemv_shape_ok(N, K, w_bit)) {
-    const size_t g = qmm::plan_gemv_lowbit(M, N, K, w_bit, group_size).workspace_bytes;
+    const size_t g =
+        qmm::plan_gemv_lowbit(M, N, K, w_bit, gemv_group(K, group_size)).workspace_bytes;
     if (g > need) need = g;
   }
   if (gemm_shape_ok(N, K, w_bit)) {
-    const size_t g = qmm::plan_gemm(M, N, K, w_bit, group_size).workspace_bytes;
+    const size_t g = qmm::plan_gemm(M, N, K, w_bit, gemm_group(K, group_size)).workspace_bytes;
     if (g > need) need = g;
   }
   return need;
 }
 
-qmm_status qmm_gemv(const void* x, const void* Q, const void* scales, const void* zeros, float* y,
-                    int M, int N, int K, int w_bit, int group_size, int x_dtype, void* workspace,
-                    size_t workspace_bytes, void* stream) {
-  const char* fn = "qmm_gemv";
+static qmm_status gemv_impl(const char* fn, const void* x, const void* Q, const void* scales,
+                            const void* zeros, void* y, int y_dtype, int M, int N, int K,
+                            int w_bit, int group_size, int x_dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   bool noop = false;
-  qmm_status st = check_matmul(fn, x, Q, scales, zeros, y, M, N, K, w_bit, group_size, x_dtype,
-                               &noop);
+  qmm_status st = check_matmul(fn, x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit, group_size,
+                               x_dtype, &noop);
   if (st != QMM_OK) return st;
   if (noop) return ok();
   if (M > 16)
@@ -195,37 +221,67 @@ qmm_status qmm_gemv(const void* x, const void* Q, const void* scales, const void
   if (!gemv_shape_ok(N, K, w_bit))
     return fail(QMM_ERR_UNSUPPORTED, "%s: needs %s", fn,
                 w_bit == 8 ? "K % 16 == 0 for int8" : "N % 4 == 0 for low-bit weights");
-  qmm::MatmulArgs a{x, Q, scales, zeros, y, M, N, K, w_bit, group_size, x_dtype, workspace,
+  const int gs = gemv_group(K, group_size);
+  qmm::MatmulArgs a{x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit, gs, -1, x_dtype, workspace,
                     reinterpret_cast<hipStream_t>(stream)};
   if (w_bit == 8) {
     const qmm::GemvInt8Plan p = qmm::plan_gemv_int8(M, N, K);
     return device_status(fn, qmm::launch_gemv_int8(a, p));
   }
-  const qmm::GemvLowbitPlan p = qmm::plan_gemv_lowbit(M, N, K, w_bit, group_size);
+  const qmm::GemvLowbitPlan p = qmm::plan_gemv_lowbit(M, N, K, w_bit, gs);
   st = check_workspace(fn, p.workspace_bytes, workspace, workspace_bytes);
   if (st != QMM_OK) return st;
   return device_status(fn, qmm::launch_gemv_lowbit(a, p));
 }
 
-qmm_status qmm_gemm(const void* x, const void* Q, const void* scales, const void* zeros, float* y,
-                    int M, int N, int K, int w_bit, int group_size, int x_dtype, void* workspace,
-                    size_t workspace_bytes, void* stream) {
-  const char* fn = "qmm_gemm";
+static qmm_status gemm_impl(const char* fn, const void* x, const void* Q, const void* scales,
+                            const void* zeros, void* y, int y_dtype, int M, int N, int K,
+                            int w_bit, int group_size, int x_dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   bool noop = false;
-  qmm_status st = check_matmul(fn, x, Q, scales, zeros, y, M, N, K, w_bit, group_size, x_dtype,
-                               &noop);
+  qmm_status st = check_matmul(fn, x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit, group_size,
+                               x_dtype, &noop);
   if (st != QMM_OK) return st;
   if (noop) return ok();
   if (!gemm_shape_ok(N, K, w_bit))
     return fail(QMM_ERR_UNSUPPORTED, "%s: tile layout needs N %% 16 == 0 and K %% %d == 0", fn,
                 qmm::mfma_kblock(w_bit));
-  const qmm::GemmPlan p = qmm::plan_gemm(M, N, K, w_bit, group_size);
+  const int gs = gemm_group(K, group_size);
+  const qmm::GemmPlan p = qmm::plan_gemm(M, N, K, w_bit, gs);
   if (p.kind < 0) return fail(QMM_ERR_UNSUPPORTED, "%s: no MFMA kernel for this shape", fn);
   st = check_workspace(fn, p.workspace_bytes, workspace, workspace_bytes);
   if (st != QMM_OK) return st;
-  qmm::MatmulArgs a{x, Q, scales, zeros, y, M, N, K, w_bit, group_size, x_dtype, workspace,
-                    reinterpret_cast<hipStream_t>(stream)};
+  qmm::MatmulArgs a{x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit, gs, group_mask(group_size),
+                    x_dtype, workspace, reinterpret_cast<hipStream_t>(stream)};
   return device_status(fn, qmm::launch_gemm(a, p));
+}
+
+qmm_status qmm_gemv(const void* x, const void* Q, const void* scales, const void* zeros, float* y,
+                    int M, int N, int K, int w_bit, int group_size, int x_dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return gemv_impl("qmm_gemv", x, Q, scales, zeros, y, QMM_F32, M, N, K, w_bit, group_size,
+                   x_dtype, workspace, workspace_bytes, stream);
+}
+
+qmm_status qmm_gemv_ex(const void* x, const void* Q, const void* scales, const void* zeros,
+                       void* y, int y_dtype, int M, int N, int K, int w_bit, int group_size,
+                       int x_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemv_impl("qmm_gemv_ex", x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit, group_size,
+                   x_dtype, workspace, workspace_bytes, stream);
+}
+
+qmm_status qmm_gemm(const void* x, const void* Q, const void* scales, const void* zeros, float* y,
+                    int M, int N, int K, int w_bit, int group_size, int x_dtype, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return gemm_impl("qmm_gemm", x, Q, scales, zeros, y, QMM_F32, M, N, K, w_bit, group_size,
+                   x_dtype, workspace, workspace_bytes, stream);
+}
+
+qmm_status qmm_gemm_ex(const void* x, const void* Q, const void* scales, const void* zeros,
+                       void* y, int y_dtype, int M, int N, int K, int w_bit, int group_size,
+                       int x_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_impl("qmm_gemm_ex", x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit, group_size,
+                   x_dtype, workspace, workspace_bytes, stream);
 }
 
 qmm_status qmm_dequant(const void* Q, int layout, const void* scales, const void* zeros,
@@ -244,7 +300,7 @@ qmm_status qmm_dequant(const void* Q, int layout, const void* scales, const void
   if (layout == QMM_LAYOUT_CANON && w_bit != 8 && K % (32 / w_bit) != 0)
     return fail(QMM_ERR_ARG, "%s: K must be a multiple of %d", fn, 32 / w_bit);
   return device_status(fn, qmm::launch_dequant(Q, layout, scales, zeros, w_out, N, K, w_bit,
-                                               group_size,
+                                               gemv_group(K, group_size),
                                                reinterpret_cast<hipStream_t>(stream)));
 }
 

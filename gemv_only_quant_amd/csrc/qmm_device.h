@@ -13,7 +13,35 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-enum { XF16 = 0, XBF16 = 1 };
+enum { XF16 = 0, XBF16 = 1, YF32 = 2 };
+
+// Runs f(yt) with y viewed as the caller's output type (float, _Float16 or
+// __bf16); stores through it convert the fp32 result once, to nearest even.
+// ydt is uniform across the launch, so the branch is taken once per call
+// site and each store loop is compiled for one type.
+template <class F>
+__device__ __forceinline__ void with_y(void* y, int ydt, F&& f);
+
+// Options carried in the top bits of a kernel's tile-count argument, so no
+// kernel needs more than 56 bytes of explicit arguments: on this runtime one
+// argument more (a 320-byte instead of a 312-byte argument segment, with the
+// hidden arguments) measured +0.3 us on every launch of a 6 us kernel.
+//   bits 0-27 tile count, bits 28-29 output type, bit 30 per-column scales
+constexpr int kTileBits = 28;
+__host__ __device__ constexpr int pack_tiles(int tiles, int ydt, bool per_column) {
+  return tiles | (ydt << kTileBits) | ((per_column ? 1 : 0) << (kTileBits + 2));
+}
+__device__ __forceinline__ int tiles_of(int t) { return t & ((1 << kTileBits) - 1); }
+__device__ __forceinline__ int ydt_of(int t) { return (t >> kTileBits) & 3; }
+// group-index mask: 0 (every group is group 0) for per-column scales
+__device__ __forceinline__ int gmask_of(int t) { return ((t >> (kTileBits + 2)) & 1) ? 0 : -1; }
+
+template <class F>
+__device__ __forceinline__ void with_y(void* y, int ydt, F&& f) {
+  if (ydt == YF32) f(reinterpret_cast<float*>(y));
+  else if (ydt == XF16) f(reinterpret_cast<_Float16*>(y));
+  else f(reinterpret_cast<__bf16*>(y));
+}
 
 // "Magic" exponent bias: OR-ing a small unsigned integer c into the low
 // mantissa bits of these 16-bit patterns gives the float B + c exactly

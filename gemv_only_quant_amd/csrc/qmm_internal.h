@@ -12,8 +12,12 @@ struct MatmulArgs {
   const void* Q;
   const void* scales;
   const void* zeros;
-  float* y;
-  int M, N, K, w_bit, group_size, x_dtype;
+  void* y;
+  int y_dtype;     // YF32, or XF16 / XBF16 (rounded once as stored)
+  int M, N, K, w_bit;
+  int group_size;  // the group size the kernel runs (K itself, or a built size, per column)
+  int group_mask;  // -1, or 0 for per-column scales: every group index masked to 0
+  int x_dtype;
   void* workspace;
   hipStream_t stream;
 };

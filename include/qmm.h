@@ -18,7 +18,11 @@
  *  - int8 weights (N, K) with the fp32 row scale applied after an fp32 sum:
  *    tiny-llm src/tinyllm/kernels/int8_gemv.py (module and int8_matmul
  *    docstrings);
- *  - the zero-size early return: marlin_cuda_kernel.cu, marlin_cuda().
+ *  - the zero-size early return: marlin_cuda_kernel.cu, marlin_cuda();
+ *  - per-column scales (one scale row, group size -1) and a 16-bit output:
+ *    marlin_cuda_kernel.cu, marlin_cuda() (groupsize -1 when the scales
+ *    have a single row) and the kernel's write-out step (the per-column
+ *    scale applied to the accumulated result as it is written in fp16).
  *
  * Conventions for every entry point
  *  - Data pointers are DEVICE pointers owned by the caller, contiguous,
@@ -40,13 +44,17 @@
  *     zeros   NULL (symmetric, z = 2^(w_bit-1): 8 for int4, 2 for int2) or
  *             (Zr, N) int32, zero of group g at bit (g % pack) * w_bit of
  *             word [g / pack][n] (fields past G are ignored)
- *     group_size in {32, 64, 128, 256}, K % group_size == 0
- *     W[k][n] = (q - z) * s[k / group_size][n]
+ *     group_size in {32, 64, 128, 256}, K % group_size == 0, or
+ *     QMM_PER_COLUMN (-1): one group spanning K -- scales (1, N), zeros
+ *     NULL or (1, N) with the zero in field 0 -- and K % 32 == 0
+ *     W[k][n] = (q - z) * s[k / group_size][n]   (per column: s[0][n])
  *   w_bit 8:
  *     Q       (N, K) int8 (two's complement), same in both layouts' inputs
  *     scales  (N,) fp32; zeros must be NULL; group_size must be 0
  *     y[m][n] = scales[n] * sum_k x[m][k] * Q[n][k]
- *   x (M, K) fp16 or bf16 (x_dtype), y (M, N) fp32, fully overwritten.
+ *   x (M, K) fp16 or bf16 (x_dtype), y (M, N) fp32, fully overwritten
+ *   (qmm_gemv_ex / qmm_gemm_ex: fp32, fp16 or bf16, the fp32 result
+ *   rounded once to nearest even).
  */
 #ifndef QMM_H
 #define QMM_H
@@ -72,7 +80,10 @@ typedef enum {
     QMM_ERR_DEVICE = 3        /* a HIP call or kernel launch failed */
 } qmm_status;
 
-typedef enum { QMM_F16 = 0, QMM_BF16 = 1 } qmm_dtype;
+typedef enum { QMM_F16 = 0, QMM_BF16 = 1, QMM_F32 = 2 } qmm_dtype;  /* x: F16 / BF16 only */
+
+/* group_size value for per-column scales and zeros (one group spanning K) */
+#define QMM_PER_COLUMN (-1)
 typedef enum { QMM_LAYOUT_CANON = 0, QMM_LAYOUT_MFMA = 1 } qmm_layout;
 
 /* Library version, (major << 16) | minor. */
@@ -134,6 +145,22 @@ QMM_API qmm_status qmm_gemv(const void* x, const void* Q, const void* scales, co
 QMM_API qmm_status qmm_gemm(const void* x, const void* Q, const void* scales, const void* zeros,
                     float* y, int M, int N, int K, int w_bit, int group_size, int x_dtype,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qmm_gemv_ex / qmm_gemm_ex: the same operations with y of type y_dtype
+ * (QMM_F32, QMM_F16 or QMM_BF16; cf. Marlin's fp16 output).  The sum is
+ * formed in fp32 exactly as in qmm_gemv / qmm_gemm and rounded once, to
+ * nearest even, as it is stored; fp16 overflows to +-inf.  An unknown
+ * y_dtype is QMM_ERR_ARG.  qmm_gemv / qmm_gemm are these with QMM_F32.
+ */
+QMM_API qmm_status qmm_gemv_ex(const void* x, const void* Q, const void* scales,
+                               const void* zeros, void* y, int y_dtype, int M, int N, int K,
+                               int w_bit, int group_size, int x_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream);
+QMM_API qmm_status qmm_gemm_ex(const void* x, const void* Q, const void* scales,
+                               const void* zeros, void* y, int y_dtype, int M, int N, int K,
+                               int w_bit, int group_size, int x_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /*
  * qmm_dequant: W (K, N) fp32 from Q in either layout, bit-exact:

@@ -16,7 +16,10 @@
  *    (the "-8 symmetric zero point" fused into its SUB/ADD constants);
  *  - int8 per-row scale applied after the sum over k, fp32 accumulation:
  *    tiny-llm src/tinyllm/kernels/int8_gemv.py, module docstring and
- *    int8_matmul() docstring.
+ *    int8_matmul() docstring;
+ *  - per-column scales, group_size -1 (one scale row, one group spanning
+ *    K): aphrodite-engine marlin_cuda_kernel.cu, marlin_cuda() (groupsize
+ *    -1 when the scales have a single row).
  *
  * Readings where the pages are silent (the zero-point packing rule, the
  * symmetric zero for int2) are listed in the project design notes.
@@ -77,8 +80,8 @@ static double x_at(const uint16_t* x, int x_dtype, int K, int m, int k) {
 static int check_lowbit(int N, int K, int w_bit, int group_size) {
     if (N < 0 || K < 0) return -1;
     if (w_bit != 2 && w_bit != 4) return -1;
-    if (group_size <= 0) return -1;
-    if (K % group_size != 0) return -1;
+    if (group_size != -1 && group_size <= 0) return -1;
+    if (group_size != -1 && K % group_size != 0) return -1;
     if (K % (32 / w_bit) != 0) return -1;
     return 0;
 }
@@ -134,7 +137,8 @@ int orc_unpack_z(const int32_t* qz, int N, int G, int w_bit, uint8_t* z_out) {
 /* c4: dequant                                                         */
 /* ------------------------------------------------------------------ */
 
-/* w = (q - z) * s, s the fp16 scale of group floor(k / group_size).
+/* w = (q - z) * s, s the fp16 scale of group floor(k / group_size), or of
+ * the single group when group_size is -1 (per-column).
  * |q - z| <= 15 needs 4 bits and s has an 11-bit significand, so the fp32
  * product is exact.  int8: w = q exactly (|q| <= 128); the fp32 row scale
  * is applied after the sum (tiny-llm int8_gemv.py docstring). */
@@ -144,7 +148,7 @@ float orc_w_at(const void* Q, const void* scales, const int32_t* zeros,
         const int8_t* q8 = (const int8_t*)Q;
         return (float)q8[(size_t)n * K + k];
     }
-    int g = k / group_size;
+    int g = group_size == -1 ? 0 : k / group_size;
     int q = (int)orc_q_at((const int32_t*)Q, N, w_bit, k, n);
     int z = (int)orc_z_at(zeros, N, w_bit, g, n);
     float s = orc_f16_to_f32(((const uint16_t*)scales)[(size_t)g * N + n]);

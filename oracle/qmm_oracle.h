@@ -16,7 +16,8 @@
  *   w_bit 2|4: Q = qw (K/pack, N) int32, pack = 32/w_bit;
  *              scales (K/group_size, N) fp16 bit patterns;
  *              zeros  NULL (symmetric, z = 2^(w_bit-1)) or
- *                     (ceil(G/pack), N) int32 packed along the group axis
+ *                     (ceil(G/pack), N) int32 packed along the group axis;
+ *              group_size -1: per column, one group spanning K (G = 1)
  *   w_bit 8:   Q (N, K) int8; scales (N,) fp32; zeros NULL; group_size 0
  * Return codes: 0 ok, -1 bad argument.
  */

@@ -27,7 +27,7 @@ class Case:
     N: int
     K: int
     w_bit: int
-    group_size: int          # 0 for int8 (per-row scale)
+    group_size: int          # 0 for int8 (per-row scale); -1 per column (one group)
     x_dtype: int             # F16 or BF16
     x: torch.Tensor          # (M, K) fp16/bf16
     Q: torch.Tensor          # int4/int2: (K/pack, N) int32; int8: (N, K) int8
@@ -72,9 +72,9 @@ def _uniform(shape, lo, hi, g):
 def lowbit_case(M, N, K, w_bit, group_size, x_dtype=F16, symmetric=False, seed=0,
                 x_std=1.0, s_lo=1e-3, s_hi=2e-2, name="lowbit"):
     """int4/int2 grouped weights: x ~ x_std*N(0,1); codes and zeros uniform;
-    fp16 scales uniform [s_lo, s_hi]."""
+    fp16 scales uniform [s_lo, s_hi].  group_size -1: per-column (G = 1)."""
     pack = 32 // w_bit
-    G = K // group_size if group_size else 0
+    G = 1 if group_size == -1 else (K // group_size if group_size else 0)
     g = torch.Generator().manual_seed(seed)
     x = (x_std * torch.randn((M, K), generator=g)).to(_TORCH_DT[x_dtype])
     Q = _words(K // pack, N, g)
@@ -98,7 +98,7 @@ def exact_lowbit_case(M, N, K, w_bit, group_size, x_dtype=F16, symmetric=False, 
     """Inputs on which every summation order is exact in fp32: x integer in
     [-3, 3]; scales 2^-(6 + (g + n) % 5), varying per group and column."""
     pack = 32 // w_bit
-    G = K // group_size
+    G = 1 if group_size == -1 else K // group_size
     g = torch.Generator().manual_seed(seed)
     x = torch.randint(-3, 4, (M, K), generator=g).to(_TORCH_DT[x_dtype])
     Q = _words(K // pack, N, g)
@@ -136,6 +136,8 @@ def workload(name):
     for M in (16, 32, 64):
         if name == f"int8_skinny_m{M}_k4096_n14336":
             return int8_case(M, 14336, 4096, BF16, seed=3000 + M, name=name)
+    if name == "int4_pc_sym_gemv_m1_k4096_n4096":  # per-column, Marlin-style symmetric
+        return lowbit_case(1, 4096, 4096, 4, -1, F16, True, seed=7000, name=name)
     if name == "int4_g128_sym_m16_k8192_n8192":
         return lowbit_case(16, 8192, 8192, 4, 128, F16, True, seed=4000, x_std=0.5, name=name)
     if name == "int4_g128_asym_smalln_m16_k14336_n1024":
@@ -150,6 +152,7 @@ def workload(name):
 WORKLOADS = [
     "int8_gemv_m1_k1024_n1024",
     "int4_g128_asym_gemv_m1_k4096_n4096",
+    "int4_pc_sym_gemv_m1_k4096_n4096",
     "int8_skinny_m16_k4096_n14336",
     "int8_skinny_m32_k4096_n14336",
     "int8_skinny_m64_k4096_n14336",

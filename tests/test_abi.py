@@ -23,7 +23,7 @@ def declared():
 
 def test_exports_every_declared_symbol():
     names = declared()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     lib = ctypes.CDLL(qmm.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -39,6 +39,8 @@ def test_version_and_sizes():
     assert qmm.qmm_packed_bytes(64, 64, 3, qmm.QMM_LAYOUT_CANON) == 0
     assert qmm.qmm_workspace_bytes(0, 64, 64, 8, 0) == 0
     assert qmm.qmm_workspace_bytes(1, 64, 100, 4, 128) == 0  # invalid: K % group
+    assert qmm.qmm_workspace_bytes(16, 4096, 4096, 4, qmm.QMM_PER_COLUMN) == 0
+    assert qmm.qmm_workspace_bytes(1, 64, 40, 4, qmm.QMM_PER_COLUMN) == 0  # K % 32
     # no built kernel needs a workspace: nothing leaves a workgroup but y
     for M, N, K, wb, g in [(1, 4096, 4096, 4, 128), (16, 14336, 4096, 8, 0),
                            (16, 8192, 8192, 4, 128), (4096, 11008, 4096, 2, 64)]:
@@ -75,6 +77,10 @@ GEMV_BAD = [
     (dict(w_bit=3), E_ARG, "w_bit"),
     (dict(x_dtype=7), E_ARG, "x_dtype"),
     (dict(group_size=0), E_ARG, "group_size"),
+    (dict(group_size=-2), E_ARG, "QMM_PER_COLUMN"),
+    (dict(group_size=-1, K=100), E_ARG, "multiple of 8"),
+    (dict(group_size=-1, K=40), E_UNS, "per-column"),
+    (dict(w_bit=8, group_size=-1), E_ARG, "per-row"),
     (dict(K=192), E_ARG, "multiple of group_size"),
     (dict(group_size=96, K=192), E_UNS, "not built"),
     (dict(w_bit=8, group_size=128), E_ARG, "per-row"),
@@ -120,6 +126,27 @@ def test_zero_size_is_noop(kw):
     assert call_gemv(**kw) == qmm.QMM_OK
     assert call_gemm(**kw) == qmm.QMM_OK
     assert qmm.qmm_last_error() == ""
+
+
+def call_ex(fn, y_dtype, **kw):
+    args = dict(x=A, Q=A, scales=A, zeros=None, y=A, M=1, N=64, K=128, w_bit=4,
+                group_size=128, x_dtype=qmm.QMM_F16)
+    args.update(kw)
+    return fn(args["x"], args["Q"], args["scales"], args["zeros"], args["y"], y_dtype,
+              args["M"], args["N"], args["K"], args["w_bit"], args["group_size"],
+              args["x_dtype"], None, 0, 0)
+
+
+@pytest.mark.parametrize("name", ["qmm_gemv_ex", "qmm_gemm_ex"])
+def test_ex_entry_points_reject(name):
+    fn = getattr(qmm._lib, name)
+    assert call_ex(fn, 3) == E_ARG and "y_dtype" in qmm.qmm_last_error()
+    assert call_ex(fn, -1) == E_ARG and name in qmm.qmm_last_error()
+    assert call_ex(fn, qmm.QMM_F16, x_dtype=qmm.QMM_F32) == E_ARG
+    assert "x_dtype" in qmm.qmm_last_error()
+    assert call_ex(fn, qmm.QMM_BF16, y=MIS) == E_ARG and "aligned" in qmm.qmm_last_error()
+    assert call_ex(fn, qmm.QMM_F16, M=0, x=None, y=None) == qmm.QMM_OK  # no-op
+    assert call_ex(fn, qmm.QMM_F16, group_size=-1, K=40) == E_UNS
 
 
 def test_layout_calls_reject():

@@ -119,7 +119,8 @@ def test_zero_m_leaves_output_untouched():
 
 # ------------------------------------------------------------ full sizes
 @pytest.mark.parametrize("name", ["int8_gemv_m1_k1024_n1024",
-                                  "int4_g128_asym_gemv_m1_k4096_n4096"])
+                                  "int4_g128_asym_gemv_m1_k4096_n4096",
+                                  "int4_pc_sym_gemv_m1_k4096_n4096"])
 def test_gemv_full_size_all_outputs(name):
     case = si.workload(name)
     y = run_gemv(case)

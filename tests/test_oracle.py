@@ -132,7 +132,7 @@ def _exact_lowbit(case):
     a = [[Fraction(0)] * N for _ in range(M)]
     for n in range(N):
         for k in range(K):
-            g = k // gs
+            g = 0 if gs == -1 else k // gs  # -1: per-column, one group
             q = _brute_code(Q[k // pack][n], k % pack, wb)
             z = (1 << (wb - 1)) if Z is None else _brute_code(Z[g // pack][n], g % pack, wb)
             w = (q - z) * Fraction(s[g][n])
@@ -177,6 +177,8 @@ LOWBIT_TINY = [
     (2, 3, 128, 2, 64, si.BF16, False),
     (3, 2, 256, 2, 128, si.F16, True),
     (1, 7, 512, 4, 32, si.F16, False),   # G = 16 > pack: two zero rows
+    (2, 5, 160, 4, -1, si.BF16, False),  # per-column: one scale row, zero in field 0
+    (3, 4, 96, 2, -1, si.F16, True),     # per-column, symmetric
 ]
 
 
@@ -185,6 +187,27 @@ def test_oracle_matches_exact_rationals_lowbit(M, N, K, w_bit, gs, xdt, sym):
     case = si.lowbit_case(M, N, K, w_bit, gs, xdt, sym, seed=M * 100 + N * 10 + w_bit)
     y, ab = oracle.qmm(*case.oracle_args())
     _assert_close_exact(y, ab, *_exact_lowbit(case))
+
+
+@pytest.mark.parametrize("w_bit,K,gs", [(4, 512, 64), (2, 512, 128), (4, 1024, 32)])
+def test_per_column_equals_grouped_with_repeated_scales(w_bit, K, gs):
+    """Per-column scales (Marlin's groupsize -1) are the grouped case whose
+    every group carries the same scale and zero: build that grouped operand
+    by repeating the single scale row and writing the zero into every field
+    of every zero word, and the oracle's results must agree bit for bit."""
+    pc = si.lowbit_case(3, 6, K, w_bit, -1, si.F16, False, seed=K + gs)
+    G, pack = K // gs, 32 // w_bit
+    scales = pc.np_scales().repeat(G, axis=0)
+    z = (pc.np_zeros()[0].astype(np.int64) & ((1 << w_bit) - 1)).astype(np.uint32)
+    word = np.zeros_like(z)
+    for f in range(pack):
+        word |= z << np.uint32(f * w_bit)
+    zeros = np.tile(word.view(np.int32), ((G + pack - 1) // pack, 1))
+    args = list(pc.oracle_args())
+    y_pc, a_pc = oracle.qmm(*args)
+    args[3], args[4], args[-1] = scales, zeros, gs
+    y_g, a_g = oracle.qmm(*args)
+    assert np.array_equal(y_pc, y_g) and np.array_equal(a_pc, a_g)
 
 
 @pytest.mark.parametrize("M,N,K,xdt", [(1, 4, 64, si.BF16), (3, 5, 96, si.F16)])
@@ -297,7 +320,8 @@ def test_mfma_pack_preserves_codes(w_bit):
 # ------------------------------------------------------- planted mistakes
 MUTATIONS = [
     ("(float)(q - z) * s", "(float)(z - q) * s"),                       # sign of zero point
-    ("int g = k / group_size;", "int g = k / group_size + (k % 2);"),   # group index
+    ("0 : k / group_size;", "0 : k / group_size + (k % 2);"),           # group index
+    ("group_size == -1 ? 0 :", "group_size == -1 ? (k & 1) :"),         # per-column group
     ("(k % pack) * w_bit", "(k / pack % pack) * w_bit"),                # unpack shift
     ("return 1u << (w_bit - 1);", "return 0u;"),                         # symmetric zero
     ("acc += p;", "acc += (k + 1 < K) ? p : 0.0;"),                      # dropped term
@@ -313,8 +337,9 @@ def test_pins_catch_planted_mistakes():
     lowbit = si.lowbit_case(2, 6, 256, 4, 64, si.F16, False, seed=21)
     lowsym = si.lowbit_case(2, 6, 256, 4, 64, si.F16, True, seed=22)
     int8c = si.int8_case(2, 5, 64, si.BF16, seed=23)
+    lowpc = si.lowbit_case(2, 6, 256, 2, -1, si.F16, False, seed=24)
     truth = [(c, _exact_lowbit(c) if c.w_bit != 8 else _exact_int8(c))
-             for c in (lowbit, lowsym, int8c)]
+             for c in (lowbit, lowsym, int8c, lowpc)]
     import ctypes
     with tempfile.TemporaryDirectory() as d:
         for old, new in MUTATIONS:
