@@ -278,6 +278,9 @@ def main():
                         "y_dtype": out_dt, "us_per_call": round(p["us"], 2),
                         "tflops": round(tf, 2), "peak_tflops": MFMA_PEAK_TFLOPS,
                         "frac": round(tf / MFMA_PEAK_TFLOPS, 4)})
+            t = traffic_for(n) if out_dt == "f32" else None
+            if t is not None:
+                pre[-1]["traffic_bytes"] = t
         out["prefill"] = pre
         out["calibration"] = calibration()
     if not args.no_cpu:
