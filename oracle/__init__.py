@@ -43,6 +43,13 @@ def lib():
         L.orc_mfma_bytes.argtypes = [I, I, I]
         L.orc_mfma_bytes.restype = S
         L.orc_mfma_pack.argtypes = [P, P, I, I, I]
+        L.orc_t2_at.argtypes = [P, I, I, I, I]
+        L.orc_i8t2_mm.argtypes = [P, P, I, I, I, P]
+        L.orc_i8t2_mm_at.argtypes = [P, P, I, I, I, I, P, P, P]
+        L.orc_t2_tile_bytes.argtypes = [I, I]
+        L.orc_t2_tile_bytes.restype = S
+        L.orc_t2_tile_locate.argtypes = [I, I, I, I, ctypes.POINTER(S), ctypes.POINTER(I)]
+        L.orc_t2_tile_pack.argtypes = [P, P, I, I]
         _lib = L
     return _lib
 
@@ -161,4 +168,45 @@ def mfma_pack(Q, N, K, w_bit):
         Q = _c(Q, np.int32)
         out = np.empty(nbytes // 4, np.int32)
     _check(lib().orc_mfma_pack(_ptr(Q), _ptr(out), N, K, w_bit), "mfma_pack")
+    return out
+
+
+# ------------------------------------------- int8 x ternary (liger-kernel page)
+def t2_at(Wp, N, K, k, n):
+    """Ternary weight value (code - 1) of element (k, n) of the packed (K/4, N) uint8."""
+    Wp = _c(Wp, np.uint8)
+    return lib().orc_t2_at(_ptr(Wp), N, K, k, n)
+
+
+def i8t2_mm(A, Wp, M, N, K):
+    """C (M, N) int32 = A (M, K) int8 times the ternary weight, exact."""
+    A, Wp = _c(A, np.int8), _c(Wp, np.uint8)
+    C = np.zeros((M, N), np.int32)
+    rc = lib().orc_i8t2_mm(_ptr(A), _ptr(Wp), M, N, K, _ptr(C))
+    if rc == -2:
+        raise ValueError("oracle i8t2_mm: a sum leaves the int32 range")
+    _check(rc, "i8t2_mm")
+    return C
+
+
+def i8t2_mm_at(A, Wp, M, N, K, ms, ns):
+    A, Wp = _c(A, np.int8), _c(Wp, np.uint8)
+    ms, ns = _c(ms, np.int32), _c(ns, np.int32)
+    C = np.zeros(ms.size, np.int32)
+    _check(lib().orc_i8t2_mm_at(_ptr(A), _ptr(Wp), M, N, K, ms.size, _ptr(ms), _ptr(ns),
+                                _ptr(C)), "i8t2_mm_at")
+    return C
+
+
+def t2_tile_locate(N, K, k, n):
+    b, sh = ctypes.c_size_t(), ctypes.c_int()
+    _check(lib().orc_t2_tile_locate(N, K, k, n, ctypes.byref(b), ctypes.byref(sh)),
+           "t2_tile_locate")
+    return b.value, sh.value
+
+
+def t2_tile_pack(Wp, N, K):
+    Wp = _c(Wp, np.uint8)
+    out = np.zeros(lib().orc_t2_tile_bytes(N, K), np.uint8)
+    _check(lib().orc_t2_tile_pack(_ptr(Wp), _ptr(out), N, K), "t2_tile_pack")
     return out

@@ -299,3 +299,89 @@ int orc_mfma_pack(const void* Q_canon, void* Q_mfma, int N, int K, int w_bit) {
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* int8 activations x ternary weights (liger-kernel, ops/experimental/  */
+/* mm_int8int2.py: pack_weights / unpack_weights / matmul)             */
+/* ------------------------------------------------------------------ */
+
+/* The packed weight has ceil(K/4) rows of N bytes.  pack_weights splits K
+ * into four consecutive quarters of R = K/4 rows (K % 4 == 0 here) and ORs
+ * quarter i into bits 2i..2i+1, so element k of column n sits in row k mod R
+ * at bit 2 * (k div R); unpack_weights masks that field and subtracts 1
+ * (codes 0, 1, 2 are the values -1, 0, +1; code 3 reads as +2). */
+int orc_t2_at(const uint8_t* Wp, int N, int K, int k, int n) {
+    int R = K / 4;
+    int code = (Wp[(size_t)(k % R) * N + n] >> (2 * (k / R))) & 3;
+    return code - 1;
+}
+
+/* C (M, N) int32 = A (M, K) int8 times the ternary W (K, N): the sum of
+ * integer products, exact (int64 accumulation, k ascending).  Returns -1 on
+ * bad sizes, -2 if a sum leaves the int32 range (the page accumulates in
+ * int32; no valid input with K < 2^23 gets there). */
+int orc_i8t2_mm(const int8_t* A, const uint8_t* Wp, int M, int N, int K, int32_t* C) {
+    if (M < 0 || N < 0 || K < 0 || K % 4 != 0) return -1;
+    int rc = 0;
+    for (int m = 0; m < M; ++m)
+        for (int n = 0; n < N; ++n) {
+            int64_t acc = 0;
+            for (int k = 0; k < K; ++k)
+                acc += (int64_t)A[(size_t)m * K + k] * orc_t2_at(Wp, N, K, k, n);
+            if (acc > INT32_MAX || acc < INT32_MIN) rc = -2;
+            C[(size_t)m * N + n] = (int32_t)acc;
+        }
+    return rc;
+}
+
+/* The same for `count` chosen outputs (ms[i], ns[i]). */
+int orc_i8t2_mm_at(const int8_t* A, const uint8_t* Wp, int M, int N, int K, int count,
+                   const int* ms, const int* ns, int32_t* C) {
+    if (M < 0 || N < 0 || K < 0 || K % 4 != 0) return -1;
+    for (int i = 0; i < count; ++i) {
+        if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N) return -1;
+        int64_t acc = 0;
+        for (int k = 0; k < K; ++k)
+            acc += (int64_t)A[(size_t)ms[i] * K + k] * orc_t2_at(Wp, N, K, k, ns[i]);
+        C[i] = (int32_t)acc;
+    }
+    return 0;
+}
+
+/* Reference permutation of the ternary weight into this library's tile
+ * layout (the HIP path's qmm_t2_pack), written from its specification:
+ *   1 KiB blocks, one per (16-column strip s, 256-deep K block kb), strip-
+ *   major; bytes [16 L, 16 L + 16) of a block belong to lane L: column
+ *   16 s + L % 16, lane group g = L / 16; dword j (0..3) of the lane holds
+ *   the 16 codes of k = 256 kb + 64 j + 16 g + e, e = 0..15, code e at bit
+ *   2 * (4 * (e % 4) + e / 4).  Codes are stored as the page stores them. */
+size_t orc_t2_tile_bytes(int N, int K) {
+    if (N < 0 || K < 0 || N % 16 || K % 256) return 0;
+    return (size_t)N * K / 4;
+}
+
+int orc_t2_tile_locate(int N, int K, int k, int n, size_t* byte, int* shift) {
+    if (orc_t2_tile_bytes(N, K) == 0 && (size_t)N * K != 0) return -1;
+    if (k < 0 || k >= K || n < 0 || n >= N) return -1;
+    int s = n / 16, kb = k / 256, r = k % 256;
+    int j = r / 64, g = (r % 64) / 16, e = r % 16;
+    int lane = 16 * g + n % 16;
+    int bit = 2 * (4 * (e % 4) + e / 4);
+    *byte = ((size_t)s * (K / 256) + kb) * 1024 + (size_t)lane * 16 + 4 * j + bit / 8;
+    *shift = bit % 8;
+    return 0;
+}
+
+int orc_t2_tile_pack(const uint8_t* Wp, uint8_t* Wt, int N, int K) {
+    size_t bytes = orc_t2_tile_bytes(N, K);
+    if (bytes == 0 && (size_t)N * K != 0) return -1;
+    memset(Wt, 0, bytes);
+    for (int k = 0; k < K; ++k)
+        for (int n = 0; n < N; ++n) {
+            size_t byte;
+            int shift;
+            orc_t2_tile_locate(N, K, k, n, &byte, &shift);
+            Wt[byte] |= (uint8_t)((orc_t2_at(Wp, N, K, k, n) + 1) << shift);
+        }
+    return 0;
+}

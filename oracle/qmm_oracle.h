@@ -19,6 +19,8 @@
  *                     (ceil(G/pack), N) int32 packed along the group axis;
  *              group_size -1: per column, one group spanning K (G = 1)
  *   w_bit 8:   Q (N, K) int8; scales (N,) fp32; zeros NULL; group_size 0
+ * and, for the int8 x ternary product (orc_i8t2_*), A (M, K) int8 and the
+ * packed ternary weight (K/4, N) uint8.
  * Return codes: 0 ok, -1 bad argument.
  */
 #ifndef QMM_ORACLE_H
@@ -67,6 +69,18 @@ int orc_qmm_at(const uint16_t* x, int x_dtype, const void* Q, const void* scales
 int orc_mfma_locate(int N, int K, int w_bit, int k, int n, size_t* byte_or_word, int* shift);
 size_t orc_mfma_bytes(int N, int K, int w_bit);
 int orc_mfma_pack(const void* Q_canon, void* Q_mfma, int N, int K, int w_bit);
+
+/* int8 activations x ternary weights (liger-kernel mm_int8int2): packed
+ * weight (K/4, N) uint8, element k at row k mod (K/4), bits 2 * (k div
+ * (K/4)), value code - 1; C (M, N) int32 exact.  K % 4 == 0. */
+int orc_t2_at(const uint8_t* Wp, int N, int K, int k, int n);
+int orc_i8t2_mm(const int8_t* A, const uint8_t* Wp, int M, int N, int K, int32_t* C);
+int orc_i8t2_mm_at(const int8_t* A, const uint8_t* Wp, int M, int N, int K, int count,
+                   const int* ms, const int* ns, int32_t* C);
+/* Reference permutation into the ternary tile layout (see the .c file). */
+size_t orc_t2_tile_bytes(int N, int K);
+int orc_t2_tile_locate(int N, int K, int k, int n, size_t* byte, int* shift);
+int orc_t2_tile_pack(const uint8_t* Wp, uint8_t* Wt, int N, int K);
 
 #ifdef __cplusplus
 }

@@ -118,6 +118,30 @@ def exact_int8_case(M, N, K, x_dtype=BF16, seed=0, name="exact_int8"):
     return Case(name, M, N, K, 8, 0, x_dtype, x, Q, scales, None)
 
 
+@dataclass
+class T2Case:
+    """int8 activations x ternary weights (the liger-kernel int8 x int2 product)."""
+    name: str
+    M: int
+    N: int
+    K: int
+    A: torch.Tensor    # (M, K) int8
+    Wp: torch.Tensor   # (K/4, N) uint8: four 2-bit codes per byte
+
+    def to(self, device):
+        return T2Case(self.name, self.M, self.N, self.K, self.A.to(device), self.Wp.to(device))
+
+
+def t2_case(M, N, K, seed=0, codes=3, name="t2"):
+    """A uniform over all int8 values; every 2-bit field of the packed weight
+    uniform over {0, .., codes-1} (3: the ternary codes; 4 also draws code 3)."""
+    g = torch.Generator().manual_seed(seed)
+    A = torch.randint(-128, 128, (M, K), dtype=torch.int64, generator=g).to(torch.int8)
+    f = torch.randint(0, codes, (K // 4, N, 4), dtype=torch.int64, generator=g)
+    Wp = (f[..., 0] | (f[..., 1] << 2) | (f[..., 2] << 4) | (f[..., 3] << 6)).to(torch.uint8)
+    return T2Case(name, M, N, K, A, Wp)
+
+
 def one_hot(case: Case, ks):
     """Copy of `case` whose x row m is the unit vector e_{ks[m]}."""
     x = torch.zeros_like(case.x)
@@ -146,6 +170,10 @@ def workload(name):
         return lowbit_case(4096, 11008, 4096, 4, 128, BF16, False, seed=5004, name=name)
     if name == "int2_g64_asym_prefill_m4096_k4096_n11008":
         return lowbit_case(4096, 11008, 4096, 2, 64, BF16, False, seed=5002, name=name)
+    if name == "i8t2_m4096_k4096_n11008":
+        return t2_case(4096, 11008, 4096, seed=8000, name=name)
+    if name == "i8t2_m16_k4096_n4096":
+        return t2_case(16, 4096, 4096, seed=8016, name=name)
     raise KeyError(name)
 
 
@@ -161,3 +189,4 @@ WORKLOADS = [
     "int4_g128_asym_prefill_m4096_k4096_n11008",
     "int2_g64_asym_prefill_m4096_k4096_n11008",
 ]
+T2_WORKLOADS = ["i8t2_m16_k4096_n4096", "i8t2_m4096_k4096_n11008"]
