@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = 2500.0       # MI355X dense fp16/bf16 matrix peak
+INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 matrix peak
 POOL_BYTES = 512 << 20          # weight pool for memory-bound workloads
 
 HEADLINE = "int4_g128_asym_gemv_m1_k4096_n4096"
@@ -50,6 +51,7 @@ PREFILL = [  # (workload, output dtype)
     ("int2_g64_asym_prefill_m4096_k4096_n11008", "f32"),
     ("int4_g128_asym_prefill_m4096_k4096_n11008", "bf16"),  # qmm_gemm_ex, bf16 y
 ]
+TERNARY = ["i8t2_m16_k4096_n4096", "i8t2_m4096_k4096_n11008"]  # int8 x ternary (qmm_i8t2_gemm)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
 CSRC = os.path.join(ROOT, "gemv_only_quant_amd", "csrc")
 
@@ -174,6 +176,53 @@ def calibration():
             "note": "measured here on plain work, for context; roofline peaks are the published ones"}
 
 
+def time_ternary(name, steps, warmup):
+    """The int8 x ternary product, timed like time_workload (weights packed
+    to the tile layout once, outside the timed region)."""
+    import torch
+    import gemv_only_quant_amd as qmm
+    import synth_inputs as si
+
+    case = si.workload(name)
+    d = case.to("cuda")
+    Wt0 = qmm.t2_pack(d.Wp, case.N, case.K)
+    wbytes = Wt0.numel()
+    tbytes = wbytes + case.M * case.K + case.M * case.N * 4
+    copies = 1 if case.M >= 1024 else max(1, -(-POOL_BYTES // wbytes))
+    pool = [Wt0] + [Wt0.clone() for _ in range(copies - 1)]
+    y = torch.empty((case.M, case.N), dtype=torch.int32, device="cuda")
+
+    def call(i):
+        qmm.qmm_i8t2_gemm(d.A, pool[i % copies], y, case.M, case.N, case.K)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(steps):
+            call(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        start.record()
+        graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        reps.append(start.elapsed_time(end) * 1e3 / steps)
+    us = statistics.median(reps)
+    del graph, pool
+    tops = 2.0 * case.M * case.N * case.K / us / 1e6
+    return {"workload": name, "entry": "qmm_i8t2_gemm", "us_per_call": round(us, 3),
+            "tops": round(tops, 2), "peak_tops": INT8_PEAK_TOPS,
+            "frac": round(tops / INT8_PEAK_TOPS, 4),
+            "weight_GBps": round(wbytes / us / 1e3, 1),
+            "hbm_frac": round(tbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
 def traffic_for(name):
     """HBM bytes per launch from the committed counter summary, if the kernel
     source it was taken with is unchanged; else None."""
@@ -282,6 +331,8 @@ def main():
             if t is not None:
                 pre[-1]["traffic_bytes"] = t
         out["prefill"] = pre
+        out["ternary"] = [time_ternary(n, 200 if n.startswith("i8t2_m16") else 10, 5)
+                          for n in TERNARY]
         out["calibration"] = calibration()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(HEADLINE)

@@ -41,13 +41,16 @@ _lib.qmm_gemm.argtypes = _MATMUL
 _lib.qmm_gemv_ex.argtypes = _MATMUL_EX
 _lib.qmm_gemm_ex.argtypes = _MATMUL_EX
 _lib.qmm_dequant.argtypes = [_P, _I, _P, _P, _P, _I, _I, _I, _I, _P]
+_lib.qmm_t2_pack.argtypes = [_P, _P, _I, _I, _P]
+_lib.qmm_t2_unpack_layout.argtypes = [_P, _P, _I, _I, _P]
+_lib.qmm_i8t2_gemm.argtypes = [_P, _P, _P, _I, _I, _I, _P]
 for _f in ("qmm_pack", "qmm_unpack_layout", "qmm_gemv", "qmm_gemm", "qmm_gemv_ex", "qmm_gemm_ex",
-           "qmm_dequant"):
+           "qmm_dequant", "qmm_t2_pack", "qmm_t2_unpack_layout", "qmm_i8t2_gemm"):
     getattr(_lib, _f).restype = _I
 
 EXPORTS = ("qmm_version", "qmm_last_error", "qmm_packed_bytes", "qmm_pack",
            "qmm_unpack_layout", "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm", "qmm_gemv_ex",
-           "qmm_gemm_ex", "qmm_dequant")
+           "qmm_gemm_ex", "qmm_dequant", "qmm_t2_pack", "qmm_t2_unpack_layout", "qmm_i8t2_gemm")
 
 
 class QmmError(ValueError):
@@ -232,3 +235,31 @@ def dequant(Q, layout, scales, zeros, N, K, w_bit, group_size):
     w = torch.empty((K, N), dtype=torch.float32, device=Q.device)
     qmm_dequant(Q, layout, scales, zeros, w, N, K, w_bit, group_size)
     return w
+
+
+# ---------------------------------------- int8 x ternary (liger-kernel product)
+def qmm_t2_pack(W_page, W_tile, N, K, stream=None):
+    _check(_lib.qmm_t2_pack(_ptr(W_page), _ptr(W_tile), N, K, _stream(stream)))
+
+
+def qmm_t2_unpack_layout(W_tile, W_page, N, K, stream=None):
+    _check(_lib.qmm_t2_unpack_layout(_ptr(W_tile), _ptr(W_page), N, K, _stream(stream)))
+
+
+def qmm_i8t2_gemm(x, W_tile, y, M, N, K, stream=None):
+    _check(_lib.qmm_i8t2_gemm(_ptr(x), _ptr(W_tile), _ptr(y), M, N, K, _stream(stream)))
+
+
+def t2_pack(W_page, N, K):
+    """(K/4, N) uint8 in the page's layout -> new tensor in the tile layout."""
+    out = torch.empty(N * K // 4, dtype=torch.uint8, device=W_page.device)
+    qmm_t2_pack(W_page, out, N, K)
+    return out
+
+
+def i8t2_gemm(x, W_tile, N, out=None):
+    """y (M, N) int32 = x (M, K) int8 times the ternary weight (tile layout)."""
+    M, K = x.shape
+    y = out if out is not None else torch.empty((M, N), dtype=torch.int32, device=x.device)
+    qmm_i8t2_gemm(x, W_tile, y, M, N, K)
+    return y

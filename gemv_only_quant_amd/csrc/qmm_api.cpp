@@ -304,4 +304,58 @@ qmm_status qmm_dequant(const void* Q, int layout, const void* scales, const void
                                                reinterpret_cast<hipStream_t>(stream)));
 }
 
+static qmm_status t2_shape(const char* fn, int N, int K, bool* noop) {
+  *noop = false;
+  if (N < 0 || K < 0) return fail(QMM_ERR_ARG, "%s: negative size N=%d K=%d", fn, N, K);
+  if (N == 0 || K == 0) {
+    *noop = true;
+    return QMM_OK;
+  }
+  if (N % 16 != 0 || K % 256 != 0)
+    return fail(QMM_ERR_UNSUPPORTED, "%s: needs N %% 16 == 0 and K %% 256 == 0 (N=%d K=%d)", fn,
+                N, K);
+  return QMM_OK;
+}
+
+static qmm_status t2_layout_call(const char* fn, const void* src, void* dst, int N, int K,
+                                 void* stream, bool to_tile) {
+  bool noop = false;
+  qmm_status st = t2_shape(fn, N, K, &noop);
+  if (st != QMM_OK) return st;
+  if (noop) return ok();
+  if (src == nullptr || dst == nullptr) return fail(QMM_ERR_ARG, "%s: NULL buffer", fn);
+  if (!aligned16(src) || !aligned16(dst))
+    return fail(QMM_ERR_ARG, "%s: buffers must be 16-byte aligned", fn);
+  const size_t bytes = (size_t)N * K / 4;
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  if (a < b + bytes && b < a + bytes) return fail(QMM_ERR_ARG, "%s: buffers overlap", fn);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return device_status(fn, to_tile ? qmm::launch_t2_pack(src, dst, N, K, s)
+                                   : qmm::launch_t2_unpack(src, dst, N, K, s));
+}
+
+qmm_status qmm_t2_pack(const void* W_page, void* W_tile, int N, int K, void* stream) {
+  return t2_layout_call("qmm_t2_pack", W_page, W_tile, N, K, stream, true);
+}
+
+qmm_status qmm_t2_unpack_layout(const void* W_tile, void* W_page, int N, int K, void* stream) {
+  return t2_layout_call("qmm_t2_unpack_layout", W_tile, W_page, N, K, stream, false);
+}
+
+qmm_status qmm_i8t2_gemm(const void* x, const void* W_tile, int32_t* y, int M, int N, int K,
+                         void* stream) {
+  const char* fn = "qmm_i8t2_gemm";
+  if (M < 0) return fail(QMM_ERR_ARG, "%s: negative M=%d", fn, M);
+  bool noop = false;
+  qmm_status st = t2_shape(fn, N, K, &noop);
+  if (st != QMM_OK) return st;
+  if (noop || M == 0) return ok();
+  if (x == nullptr || W_tile == nullptr || y == nullptr)
+    return fail(QMM_ERR_ARG, "%s: NULL x, W_tile or y", fn);
+  if (!aligned16(x) || !aligned16(W_tile) || !aligned16(y))
+    return fail(QMM_ERR_ARG, "%s: x, W_tile and y must be 16-byte aligned", fn);
+  return device_status(fn, qmm::launch_i8t2_gemm(x, W_tile, y, M, N, K,
+                                                 reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -63,6 +63,12 @@ struct GemmPlan {
 GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size);
 hipError_t launch_gemm(const MatmulArgs& a, const GemmPlan& p);
 
+// ---- int8 x ternary (ternary.hip) -----------------------------------------
+hipError_t launch_t2_pack(const void* Wp, void* Wt, int N, int K, hipStream_t s);
+hipError_t launch_t2_unpack(const void* Wt, void* Wp, int N, int K, hipStream_t s);
+hipError_t launch_i8t2_gemm(const void* x, const void* Wt, int32_t* y, int M, int N, int K,
+                            hipStream_t s);
+
 // Optional integer override from the environment (tile sweeps); -1 if unset.
 int env_int(const char* name);
 

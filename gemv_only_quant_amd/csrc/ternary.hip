@@ -1,0 +1,239 @@
+// ternary.hip -- int8 activations x ternary weights on the int8 matrix cores
+// (liger-kernel ops/experimental/mm_int8int2.py: matmul of int8 A by weights
+// in {-1, 0, +1} stored as 2-bit codes value + 1, int32 accumulation).
+//
+// Page layout of the weight (pack_weights): (K/4, N) uint8, K split into four
+// consecutive quarters of R = K/4 rows, quarter i in bits 2i..2i+1, so
+// element k of column n is code (Wp[k mod R][n] >> 2 (k div R)) & 3.  A lane
+// of an MFMA needs 16 consecutive k of one column, which that layout spreads
+// over 16 rows N bytes apart; qmm_t2_pack therefore rewrites it once into the
+// tile layout below, and the GEMM streams that:
+//  * 1 KiB blocks, one per (16-column strip, 256-deep K block), strip-major;
+//    bytes [16 L, 16 L + 16) are lane L: column 16 s + L % 16, lane group
+//    g = L / 16; dword j holds the 16 codes of k = 256 kb + 64 j + 16 g + e,
+//    code e at bit 2 (4 (e % 4) + e / 4), so (w >> 2t) & 0x03030303 is codes
+//    4t .. 4t + 3 in byte order;
+//  * one v_perm_b32 per 4 codes maps code c to the int8 c - 1 through the
+//    table {-1, 0, +1, +2} -- the page's "mask, shift, subtract 1" -- giving
+//    the B operand of v_mfma_i32_16x16x64_i8 directly (the x operand uses the
+//    same k order per lane group, so products pair up whatever order the
+//    instruction sums in);
+//  * x tiles go global -> LDS (global_load_lds_dwordx4), double-buffered and
+//    fragment-major (one 1 KiB block per 16 rows x 64 k), so every A operand
+//    is one conflict-free ds_read_b128; the sums are exact int32.
+#include <hip/hip_runtime.h>
+
+#include "qmm_device.h"
+#include "qmm_internal.h"
+
+namespace qmm {
+
+// bit position of code e (0..15) inside a dword of the tile layout
+__host__ __device__ constexpr int t2_pos(int e) { return 2 * (4 * (e % 4) + e / 4); }
+
+// code of element (k, n) in the page layout
+__device__ __forceinline__ uint32_t t2_code(const uint8_t* Wp, int N, int R, int k, int n) {
+  return (Wp[(size_t)(k % R) * N + n] >> (2 * (k / R))) & 3u;
+}
+
+// One thread per output dword of the tile layout (dword t = block * 256 +
+// lane * 4 + j).
+__global__ void t2_pack_kernel(const uint8_t* __restrict__ Wp, uint32_t* __restrict__ Wt, int N,
+                               int K) {
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const int nkb = K / 256;
+  const size_t total = (size_t)N * K / 16;
+  if (t >= total) return;
+  const int j = (int)(t % 4), lane = (int)((t / 4) % 64);
+  const size_t blk = t / 256;
+  const int s = (int)(blk / nkb), kb = (int)(blk % nkb);
+  const int n = 16 * s + lane % 16, g = lane / 16;
+  const int R = K / 4;
+  uint32_t w = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) w |= t2_code(Wp, N, R, 256 * kb + 64 * j + 16 * g + e, n) << t2_pos(e);
+  Wt[t] = w;
+}
+
+// Inverse: one thread per page byte (row r, column n), four quarters.
+__global__ void t2_unpack_kernel(const uint32_t* __restrict__ Wt, uint8_t* __restrict__ Wp, int N,
+                                 int K) {
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const int R = K / 4;
+  if (t >= (size_t)R * N) return;
+  const int r = (int)(t / N), n = (int)(t % N);
+  const int nkb = K / 256, s = n / 16;
+  uint32_t b = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int k = i * R + r;
+    const int kb = k / 256, rr = k % 256, j = rr / 64, g = (rr % 64) / 16, e = rr % 16;
+    const uint32_t w = Wt[((size_t)s * nkb + kb) * 256 + (16 * g + n % 16) * 4 + j];
+    b |= ((w >> t2_pos(e)) & 3u) << (2 * i);
+  }
+  Wp[t] = (uint8_t)b;
+}
+
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+// the 16 int8 weights of one k step (dword w of a lane's slot)
+__device__ __forceinline__ u32x4_t t2_operand(uint32_t w) {
+  u32x4_t b;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    b[t] = __builtin_amdgcn_perm(0u, 0x020100FFu, (w >> (2 * t)) & 0x03030303u);
+  return b;
+}
+
+// Workgroup tile 16 MT rows x 64 NT4 columns: 4 waves side by side along N,
+// each NT4 strips of 16 columns, MT 16-row tiles; 256-deep stages.
+template <int MT, int NT4>
+__global__ __launch_bounds__(256) void i8t2_gemm_kernel(const int8_t* __restrict__ x,
+                                                        const u32x4_t* __restrict__ Wt,
+                                                        int32_t* __restrict__ y, int M, int N,
+                                                        int K, int n_tiles) {
+  constexpr int STEPS = 4;              // 64-deep MFMA steps per stage
+  constexpr int FRAGS = MT * STEPS;     // 1 KiB x fragments per stage
+  constexpr int XPW = FRAGS / 4;        // fragments each wave loads
+  static_assert(FRAGS % 4 == 0, "the 4 waves share the x fragments evenly");
+  __shared__ u32x4_t xa[2][FRAGS * 64];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+  const int l16 = lane & 15, quad = lane >> 4;
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int nt = w % n_tiles, m0 = (w / n_tiles) * 16 * MT;
+  const int strips = N / 16, nkb = K / 256;
+  const int s0 = (nt * 4 + wave) * NT4;
+  int sidx[NT4];
+#pragma unroll
+  for (int s = 0; s < NT4; ++s) sidx[s] = min(s0 + s, strips - 1);  // loads stay in bounds
+  const int rows_left = M - 1 - m0;
+
+  // x fragment f (row tile f / STEPS, k step f % STEPS): lane p holds row
+  // 16 (f / STEPS) + p % 16, bytes k = 64 (f % STEPS) + 16 (p / 16) .. + 15;
+  // rows past M read row M - 1 (never stored)
+  auto load_x = [&](int st, int buf) {
+#pragma unroll
+    for (int j = 0; j < XPW; ++j) {
+      const int f = wave * XPW + j;
+      const int rr = min(16 * (f / STEPS) + l16, rows_left);
+      const int k = st * 256 + 64 * (f % STEPS) + 16 * quad;
+      __builtin_amdgcn_global_load_lds((const void*)(x + (size_t)(m0 + rr) * K + k),
+                                       (__attribute__((address_space(3))) void*)(&xa[buf][f * 64]),
+                                       16, 0, 0);
+    }
+  };
+  auto load_w = [&](int st, u32x4_t (&R)[NT4]) {
+#pragma unroll
+    for (int s = 0; s < NT4; ++s) R[s] = Wt[((size_t)sidx[s] * nkb + st) * 64 + lane];
+  };
+
+  i32x4_t acc[MT][NT4];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int s = 0; s < NT4; ++s) acc[i][s] = i32x4_t{0, 0, 0, 0};
+
+  // One stage: MFMAs on the x tile in xa[st & 1] and the weights in `use`,
+  // while the next stage's weights go to `fill` and its x tile to the other
+  // buffer (the last stage re-reads itself, keeping the body branch-free).
+  // Two register sets take turns (no loop-carried copy: a copy would be
+  // scheduled right behind the loads and stall the stage on them).
+  auto stage = [&](int st, const u32x4_t (&use)[NT4], u32x4_t (&fill)[NT4]) {
+    const int buf = st & 1;
+    const int stn = min(st + 1, nkb - 1);
+    u32x4_t b[NT4];
+#pragma unroll
+    for (int s = 0; s < NT4; ++s) b[s] = t2_operand(use[s][0]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(stn, fill);
+    load_x(stn, buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const u32x4_t* xs = &xa[buf][0];
+#pragma unroll
+    for (int j = 0; j < STEPS; ++j) {
+      u32x4_t bn[NT4];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        const u32x4_t a = xs[(i * STEPS + j) * 64 + lane];
+#pragma unroll
+        for (int s = 0; s < NT4; ++s)
+          acc[i][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a),
+                                                            __builtin_bit_cast(i32x4_t, b[s]),
+                                                            acc[i][s], 0, 0, 0);
+        // next k step's operands, spread over the row tiles
+        if (j + 1 < STEPS) {
+#pragma unroll
+          for (int s = 0; s < NT4; ++s)
+            if (i == s % MT) bn[s] = t2_operand(use[s][j + 1]);
+        }
+      }
+      if (j + 1 < STEPS) {
+#pragma unroll
+        for (int s = 0; s < NT4; ++s) b[s] = bn[s];
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // the next stage's loads, this wave's
+    __syncthreads();                      // ... and every wave's x tile
+  };
+
+  u32x4_t wa[NT4], wb[NT4];
+  load_x(0, 0);
+  load_w(0, wa);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  for (int st = 0; st < nkb; st += 2) {
+    stage(st, wa, wb);
+    if (st + 1 < nkb) stage(st + 1, wb, wa);
+  }
+
+#pragma unroll
+  for (int s = 0; s < NT4; ++s) {
+    if (s0 + s >= strips) continue;
+    const int n = 16 * (s0 + s) + l16;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 16 * i + 4 * quad + r;
+        if (m < M) y[(size_t)m * N + n] = acc[i][s][r];
+      }
+  }
+}
+
+// ---------------------------------------------------------------- host side
+hipError_t launch_t2_pack(const void* Wp, void* Wt, int N, int K, hipStream_t st) {
+  const size_t total = (size_t)N * K / 16;
+  hipLaunchKernelGGL(t2_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<const uint8_t*>(Wp), reinterpret_cast<uint32_t*>(Wt), N, K);
+  return hipGetLastError();
+}
+
+hipError_t launch_t2_unpack(const void* Wt, void* Wp, int N, int K, hipStream_t st) {
+  const size_t total = (size_t)N * K / 4;
+  hipLaunchKernelGGL(t2_unpack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                     reinterpret_cast<const uint32_t*>(Wt), reinterpret_cast<uint8_t*>(Wp), N, K);
+  return hipGetLastError();
+}
+
+template <int MT, int NT4>
+static hipError_t launch_i8t2(const void* x, const void* Wt, int32_t* y, int M, int N, int K,
+                              hipStream_t st) {
+  const int strips = N / 16;
+  const int n_tiles = (strips + 4 * NT4 - 1) / (4 * NT4);
+  const int m_tiles = (M + 16 * MT - 1) / (16 * MT);
+  hipLaunchKernelGGL((i8t2_gemm_kernel<MT, NT4>), dim3((unsigned)(n_tiles * m_tiles)), dim3(256), 0,
+                     st, reinterpret_cast<const int8_t*>(x), reinterpret_cast<const u32x4_t*>(Wt),
+                     y, M, N, K, n_tiles);
+  return hipGetLastError();
+}
+
+hipError_t launch_i8t2_gemm(const void* x, const void* Wt, int32_t* y, int M, int N, int K,
+                            hipStream_t st) {
+  // decode-sized M: one 16-row tile and one strip per wave (more workgroups)
+  if (M <= 16) return launch_i8t2<1, 1>(x, Wt, y, M, N, K, st);
+  return launch_i8t2<8, 4>(x, Wt, y, M, N, K, st);
+}
+
+}  // namespace qmm

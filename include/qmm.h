@@ -60,6 +60,7 @@
 #define QMM_H
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -169,6 +170,35 @@ QMM_API qmm_status qmm_gemm_ex(const void* x, const void* Q, const void* scales,
  */
 QMM_API qmm_status qmm_dequant(const void* Q, int layout, const void* scales, const void* zeros,
                        float* w_out, int N, int K, int w_bit, int group_size, void* stream);
+
+/*
+ * int8 activations x ternary weights (liger-kernel ops/experimental/
+ * mm_int8int2.py): y (M, N) int32 = x (M, K) int8 times W (K, N) with
+ * values in {-1, 0, +1}, exact.  The page stores W as pack_weights does:
+ * (K/4, N) uint8, K split into four consecutive quarters of R = K/4 rows,
+ * quarter i in bits 2i..2i+1, each field the value + 1 (code 3 reads as +2,
+ * as unpack_weights's "mask, shift, minus 1" gives).
+ *
+ * qmm_t2_pack rewrites that once into the tile layout qmm_i8t2_gemm reads:
+ * 1 KiB blocks, one per (16-column strip s, 256-deep K block kb),
+ * strip-major; bytes [16 L, 16 L + 16) of a block are lane L: column
+ * 16 s + L % 16, lane group g = L / 16; dword j (0..3) of the lane holds
+ * the codes of k = 256 kb + 64 j + 16 g + e, e = 0..15, code e at bit
+ * 2 (4 (e % 4) + e / 4).  Both layouts take N * K / 4 bytes.  Requires
+ * N % 16 == 0 and K % 256 == 0 (else QMM_ERR_UNSUPPORTED); buffers must
+ * not overlap.  qmm_t2_unpack_layout is the exact inverse.
+ */
+QMM_API qmm_status qmm_t2_pack(const void* W_page, void* W_tile, int N, int K, void* stream);
+QMM_API qmm_status qmm_t2_unpack_layout(const void* W_tile, void* W_page, int N, int K,
+                                        void* stream);
+/*
+ * qmm_i8t2_gemm: y = x * W on the int8 matrix cores, W in the tile layout;
+ * any M >= 1, N % 16 == 0, K % 256 == 0; y fully overwritten.  The sums are
+ * exact for K < 2^23 (|x w| <= 256); larger K wraps as the page's int32
+ * accumulator would.
+ */
+QMM_API qmm_status qmm_i8t2_gemm(const void* x, const void* W_tile, int32_t* y, int M, int N,
+                                 int K, void* stream);
 
 #ifdef __cplusplus
 }

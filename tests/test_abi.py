@@ -23,7 +23,7 @@ def declared():
 
 def test_exports_every_declared_symbol():
     names = declared()
-    assert len(names) == 11, names
+    assert len(names) == 14, names
     lib = ctypes.CDLL(qmm.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -147,6 +147,21 @@ def test_ex_entry_points_reject(name):
     assert call_ex(fn, qmm.QMM_BF16, y=MIS) == E_ARG and "aligned" in qmm.qmm_last_error()
     assert call_ex(fn, qmm.QMM_F16, M=0, x=None, y=None) == qmm.QMM_OK  # no-op
     assert call_ex(fn, qmm.QMM_F16, group_size=-1, K=40) == E_UNS
+
+
+def test_ternary_calls_reject():
+    L = qmm._lib
+    assert L.qmm_t2_pack(A, A + 64, 64, 256, 0) == E_ARG and "overlap" in qmm.qmm_last_error()
+    assert L.qmm_t2_pack(A, None, 64, 256, 0) == E_ARG
+    assert L.qmm_t2_pack(A, 0x100000, 24, 256, 0) == E_UNS and "N % 16" in qmm.qmm_last_error()
+    assert L.qmm_t2_unpack_layout(A, 0x100000, 64, 128, 0) == E_UNS          # K % 256
+    assert L.qmm_t2_pack(A, A, 0, 256, 0) == qmm.QMM_OK                      # empty
+    assert L.qmm_t2_pack(MIS, 0x100000, 64, 256, 0) == E_ARG
+    assert L.qmm_i8t2_gemm(A, A, A, -1, 64, 256, 0) == E_ARG
+    assert L.qmm_i8t2_gemm(A, A, None, 4, 64, 256, 0) == E_ARG
+    assert L.qmm_i8t2_gemm(A, A, MIS, 4, 64, 256, 0) == E_ARG
+    assert L.qmm_i8t2_gemm(A, A, A, 4, 64, 320, 0) == E_UNS
+    assert L.qmm_i8t2_gemm(None, None, None, 0, 64, 256, 0) == qmm.QMM_OK   # M = 0
 
 
 def test_layout_calls_reject():
