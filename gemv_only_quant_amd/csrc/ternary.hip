@@ -202,6 +202,72 @@ __global__ __launch_bounds__(256) void i8t2_gemm_kernel(const int8_t* __restrict
   }
 }
 
+// Decode-sized M (one 16-row tile): a workgroup owns NT strips, and its 4
+// waves split K into quarters (as the skinny low-bit GEMM does), each with
+// up to 4 stages of weight slots and x fragments in flight straight to
+// registers; the 4 partial tiles meet in LDS.
+template <int NT>
+__global__ __launch_bounds__(256) void i8t2_skinny_kernel(const int8_t* __restrict__ x,
+                                                          const u32x4_t* __restrict__ Wt,
+                                                          int32_t* __restrict__ y, int M, int N,
+                                                          int K, int n_tiles) {
+  constexpr int DEPTH = 4;  // stages in flight per wave
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l16 = lane & 15, quad = lane >> 4;
+  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int nt = w % n_tiles, m0 = (w / n_tiles) * 16;
+  const int strips = N / 16, nkb = K / 256;
+  const int s0 = nt * NT;
+  int sidx[NT];
+#pragma unroll
+  for (int s = 0; s < NT; ++s) sidx[s] = min(s0 + s, strips - 1);
+  const int per = (nkb + 3) / 4;
+  const int kb0 = min(nkb, wave * per), kb1 = min(nkb, kb0 + per);
+  const int8_t* xrow = x + (size_t)min(m0 + l16, M - 1) * K + 16 * quad;
+
+  i32x4_t acc[NT];
+#pragma unroll
+  for (int s = 0; s < NT; ++s) acc[s] = i32x4_t{0, 0, 0, 0};
+  for (int kb = kb0; kb < kb1; kb += DEPTH) {
+    u32x4_t wr[DEPTH][NT], xr[DEPTH][4];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int k = min(kb + d, kb1 - 1);  // past the range: re-read, not used
+#pragma unroll
+      for (int s = 0; s < NT; ++s) wr[d][s] = Wt[((size_t)sidx[s] * nkb + k) * 64 + lane];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xr[d][j] = *reinterpret_cast<const u32x4_t*>(xrow + (size_t)k * 256 + 64 * j);
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      if (kb + d < kb1) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int s = 0; s < NT; ++s)
+            acc[s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                __builtin_bit_cast(i32x4_t, xr[d][j]),
+                __builtin_bit_cast(i32x4_t, t2_operand(wr[d][s][j])), acc[s], 0, 0, 0);
+      }
+    }
+  }
+
+  __shared__ int32_t red[4][16][16 * NT + 1];
+#pragma unroll
+  for (int s = 0; s < NT; ++s)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][4 * quad + r][16 * s + l16] = acc[s][r];
+  __syncthreads();
+  for (int o = threadIdx.x; o < 16 * 16 * NT; o += 256) {
+    const int rr = o / (16 * NT), cc = o % (16 * NT);
+    const int m = m0 + rr, n = 16 * s0 + cc;
+    if (m < M && n < N) y[(size_t)m * N + n] = red[0][rr][cc] + red[1][rr][cc] + red[2][rr][cc] +
+                                               red[3][rr][cc];
+  }
+}
+
 // ---------------------------------------------------------------- host side
 hipError_t launch_t2_pack(const void* Wp, void* Wt, int N, int K, hipStream_t st) {
   const size_t total = (size_t)N * K / 16;
@@ -231,8 +297,15 @@ static hipError_t launch_i8t2(const void* x, const void* Wt, int32_t* y, int M, 
 
 hipError_t launch_i8t2_gemm(const void* x, const void* Wt, int32_t* y, int M, int N, int K,
                             hipStream_t st) {
-  // decode-sized M: one 16-row tile and one strip per wave (more workgroups)
-  if (M <= 16) return launch_i8t2<1, 1>(x, Wt, y, M, N, K, st);
+  if (M <= 16) {
+    // one strip per workgroup; K split over its 4 waves
+    const int n_tiles = N / 16;
+    hipLaunchKernelGGL((i8t2_skinny_kernel<1>), dim3((unsigned)n_tiles), dim3(256), 0, st,
+                       reinterpret_cast<const int8_t*>(x), reinterpret_cast<const u32x4_t*>(Wt), y,
+                       M, N, K, n_tiles);
+    return hipGetLastError();
+  }
+  if (M <= 64) return launch_i8t2<1, 1>(x, Wt, y, M, N, K, st);
   return launch_i8t2<8, 4>(x, Wt, y, M, N, K, st);
 }
 
