@@ -50,6 +50,9 @@ def lib():
         L.orc_t2_tile_bytes.restype = S
         L.orc_t2_tile_locate.argtypes = [I, I, I, I, ctypes.POINTER(S), ctypes.POINTER(I)]
         L.orc_t2_tile_pack.argtypes = [P, P, I, I]
+        L.orc_f32_to_f16.argtypes = [ctypes.c_float]
+        L.orc_f32_to_f16.restype = ctypes.c_uint16
+        L.orc_rtn_quantize.argtypes = [P, I, I, I, I, I, P, P, P]
         _lib = L
     return _lib
 
@@ -210,3 +213,25 @@ def t2_tile_pack(Wp, N, K):
     out = np.zeros(lib().orc_t2_tile_bytes(N, K), np.uint8)
     _check(lib().orc_t2_tile_pack(_ptr(Wp), _ptr(out), N, K), "t2_tile_pack")
     return out
+
+
+# --------------------------------------------- round-to-nearest quantizer
+def f32_to_f16(values):
+    """fp16 bit patterns of fp32 values, round to nearest even."""
+    L = lib()
+    v = np.asarray(values, np.float32).ravel()
+    return np.array([L.orc_f32_to_f16(float(a)) for a in v], np.uint16)
+
+
+def rtn_quantize(W, N, K, w_bit, group_size, symmetric):
+    """W (K, N) fp32 -> (qw (K/pack, N) int32, scales (G, N) fp16 bits,
+    qzeros (ceil(G/pack), N) int32 or None)."""
+    W = _c(W, np.float32)
+    pack = 32 // w_bit
+    G = 1 if group_size == -1 else K // group_size
+    qw = np.zeros((K // pack, N), np.int32)
+    sc = np.zeros((G, N), np.uint16)
+    qz = None if symmetric else np.zeros(((G + pack - 1) // pack, N), np.int32)
+    _check(lib().orc_rtn_quantize(_ptr(W), N, K, w_bit, group_size, int(symmetric), _ptr(qw),
+                                  _ptr(sc), _ptr(qz)), "rtn_quantize")
+    return qw, sc, qz

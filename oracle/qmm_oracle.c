@@ -385,3 +385,93 @@ int orc_t2_tile_pack(const uint8_t* Wp, uint8_t* Wt, int N, int K) {
         }
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* Round-to-nearest quantizer (the step before the path: fp weights ->  */
+/* qw, scales, qzeros in the operand contract of BitDistiller's         */
+/* quant_matmul_kernel; the page gives only those shapes)               */
+/* ------------------------------------------------------------------ */
+
+/* fp32 -> fp16 bit pattern, round to nearest even, from the binary16
+ * definition: normals 2^(e-15) (1 + m/1024), e in 1..30; subnormals
+ * 2^-14 (m/1024); magnitudes that round past 65504 become infinity. */
+uint16_t orc_f32_to_f16(float f) {
+    uint16_t sign = signbit(f) ? 0x8000u : 0u;
+    double a = fabs((double)f);
+    if (isnan(f)) return (uint16_t)(sign | 0x7E00u);
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);                 /* a = fr * 2^e, fr in [0.5, 1) */
+    int ue = e - 1;               /* a in [2^ue, 2^(ue+1)) */
+    if (ue < -14) ue = -14;       /* subnormal range: spacing 2^-24 */
+    double ulp = ldexp(1.0, ue - 10);
+    double n = rint(a / ulp);     /* exact quotient (power-of-two divisor), ties to even */
+    double v = n * ulp;           /* the rounded magnitude */
+    if (v >= 65536.0) return (uint16_t)(sign | 0x7C00u);  /* rounds past the largest finite */
+    if (v < ldexp(1.0, -14))      /* subnormal (or rounded up to the smallest normal below) */
+        return (uint16_t)(sign | (uint16_t)rint(v / ldexp(1.0, -24)));
+    int ve;
+    double vf = frexp(v, &ve);    /* v = vf * 2^ve, vf in [0.5, 1) */
+    int exp16 = ve - 1 + 15;
+    uint16_t mant = (uint16_t)rint((vf * 2.0 - 1.0) * 1024.0);
+    return (uint16_t)(sign | (uint16_t)(exp16 << 10) | mant);
+}
+
+/* Quantize W (K, N) fp32, group by group along k, column by column, with
+ * min = min(0, min w) and max = max(0, max w) (the range holds 0, so zero is
+ * exactly representable and a constant group keeps its value to half a
+ * step):
+ *   asymmetric: s = (max - min) / (2^b - 1), z = clamp(rint(-min / s), 0, 2^b - 1)
+ *   symmetric:  s = max(|max|, |min|) / (2^(b-1) - 1), z = 2^(b-1)
+ *   q = clamp(rint(w / s) + z, 0, 2^b - 1)
+ * with s stored as fp16 (round to nearest even; if that is 0 -- an all-zero
+ * group -- s = 1) and the codes computed from the stored scale, every step
+ * in fp32 (division correctly rounded, rint ties to even).
+ * group_size -1: one group spanning K.  Outputs in the canonical layout:
+ * qw (K/pack, N), scales (G, N), qzeros (ceil(G/pack), N) (not written when
+ * symmetric). */
+int orc_rtn_quantize(const float* W, int N, int K, int w_bit, int group_size, int symmetric,
+                     int32_t* qw, uint16_t* scales, int32_t* qzeros) {
+    if (check_lowbit(N, K, w_bit, group_size)) return -1;
+    int gs = group_size == -1 ? K : group_size;
+    int G = gs ? K / gs : 0, pack = 32 / w_bit;
+    float qmax = (float)((1 << w_bit) - 1);
+    memset(qw, 0, (size_t)(K / pack) * N * sizeof(int32_t));
+    if (!symmetric) memset(qzeros, 0, (size_t)((G + pack - 1) / pack) * N * sizeof(int32_t));
+    for (int n = 0; n < N; ++n) {
+        for (int g = 0; g < G; ++g) {
+            float mn = 0.0f, mx = 0.0f;
+            for (int i = 0; i < gs; ++i) {
+                float v = W[((size_t)g * gs + i) * N + n];
+                if (v < mn) mn = v;
+                if (v > mx) mx = v;
+            }
+            float s32;
+            if (symmetric) {
+                float amax = fabsf(mx) > fabsf(mn) ? fabsf(mx) : fabsf(mn);
+                s32 = amax / (float)((1 << (w_bit - 1)) - 1);
+            } else {
+                s32 = (mx - mn) / qmax;
+            }
+            uint16_t sb = orc_f32_to_f16(s32);
+            if ((sb & 0x7FFFu) == 0) sb = 0x3C00u; /* 1.0 */
+            scales[(size_t)g * N + n] = sb;
+            float s = orc_f16_to_f32(sb);
+            float z;
+            if (symmetric) {
+                z = (float)(1 << (w_bit - 1));
+            } else {
+                z = rintf(-mn / s);
+                z = z < 0.0f ? 0.0f : (z > qmax ? qmax : z);
+                qzeros[(size_t)(g / pack) * N + n] |= (int32_t)((uint32_t)z << ((g % pack) * w_bit));
+            }
+            for (int i = 0; i < gs; ++i) {
+                int k = g * gs + i;
+                float q = rintf(W[(size_t)k * N + n] / s) + z;
+                q = q < 0.0f ? 0.0f : (q > qmax ? qmax : q);
+                qw[(size_t)(k / pack) * N + n] |= (int32_t)((uint32_t)q << ((k % pack) * w_bit));
+            }
+        }
+    }
+    return 0;
+}

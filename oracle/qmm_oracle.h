@@ -82,6 +82,12 @@ size_t orc_t2_tile_bytes(int N, int K);
 int orc_t2_tile_locate(int N, int K, int k, int n, size_t* byte, int* shift);
 int orc_t2_tile_pack(const uint8_t* Wp, uint8_t* Wt, int N, int K);
 
+/* fp32 -> fp16 bits, round to nearest even (from the binary16 definition). */
+uint16_t orc_f32_to_f16(float f);
+/* Round-to-nearest quantizer into the canonical operands (see the .c file). */
+int orc_rtn_quantize(const float* W /*(K,N)*/, int N, int K, int w_bit, int group_size,
+                     int symmetric, int32_t* qw, uint16_t* scales, int32_t* qzeros);
+
 #ifdef __cplusplus
 }
 #endif
