@@ -223,6 +223,46 @@ def time_ternary(name, steps, warmup):
             "hbm_frac": round(tbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
 
 
+def time_quantize(K, N, w_bit, group_size, steps=20):
+    """qmm_quantize of a (K, N) fp16 weight (0.02 N(0,1)), graph-replayed.
+    Bytes: the fp16 input (read once; the kernel's second pass hits cache)
+    plus the packed outputs."""
+    import torch
+    import gemv_only_quant_amd as qmm
+
+    g = torch.Generator().manual_seed(9000)
+    W = (0.02 * torch.randn((K, N), generator=g)).half().cuda()
+    pack = 32 // w_bit
+    G = K // group_size
+    qw = torch.empty((K // pack, N), dtype=torch.int32, device="cuda")
+    sc = torch.empty((G, N), dtype=torch.float16, device="cuda")
+    qz = torch.empty(((G + pack - 1) // pack, N), dtype=torch.int32, device="cuda")
+    call = lambda: qmm.qmm_quantize(W, qmm.QMM_F16, qw, sc, qz, N, K, w_bit, group_size, False)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            call()
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        a.record()
+        graph.replay()
+        b.record()
+        torch.cuda.synchronize()
+        reps.append(a.elapsed_time(b) * 1e3 / steps)
+    us = statistics.median(reps)
+    nbytes = W.numel() * 2 + qw.numel() * 4 + sc.numel() * 2 + qz.numel() * 4
+    return {"workload": f"rtn_int{w_bit}_g{group_size}_fp16_k{K}_n{N}", "entry": "qmm_quantize",
+            "us_per_call": round(us, 2), "GBps": round(nbytes / us / 1e3, 1),
+            "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
 def traffic_for(name):
     """HBM bytes per launch from the committed counter summary, if the kernel
     source it was taken with is unchanged; else None."""
@@ -333,6 +373,7 @@ def main():
         out["prefill"] = pre
         out["ternary"] = [time_ternary(n, 200 if n.startswith("i8t2_m16") else 10, 5)
                           for n in TERNARY]
+        out["quantize"] = [time_quantize(4096, 4096, 4, 128)]
         out["calibration"] = calibration()
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(HEADLINE)

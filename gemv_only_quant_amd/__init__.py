@@ -44,13 +44,15 @@ _lib.qmm_dequant.argtypes = [_P, _I, _P, _P, _P, _I, _I, _I, _I, _P]
 _lib.qmm_t2_pack.argtypes = [_P, _P, _I, _I, _P]
 _lib.qmm_t2_unpack_layout.argtypes = [_P, _P, _I, _I, _P]
 _lib.qmm_i8t2_gemm.argtypes = [_P, _P, _P, _I, _I, _I, _P]
+_lib.qmm_quantize.argtypes = [_P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P]
 for _f in ("qmm_pack", "qmm_unpack_layout", "qmm_gemv", "qmm_gemm", "qmm_gemv_ex", "qmm_gemm_ex",
-           "qmm_dequant", "qmm_t2_pack", "qmm_t2_unpack_layout", "qmm_i8t2_gemm"):
+           "qmm_dequant", "qmm_t2_pack", "qmm_t2_unpack_layout", "qmm_i8t2_gemm", "qmm_quantize"):
     getattr(_lib, _f).restype = _I
 
 EXPORTS = ("qmm_version", "qmm_last_error", "qmm_packed_bytes", "qmm_pack",
            "qmm_unpack_layout", "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm", "qmm_gemv_ex",
-           "qmm_gemm_ex", "qmm_dequant", "qmm_t2_pack", "qmm_t2_unpack_layout", "qmm_i8t2_gemm")
+           "qmm_gemm_ex", "qmm_dequant", "qmm_t2_pack", "qmm_t2_unpack_layout", "qmm_i8t2_gemm",
+           "qmm_quantize")
 
 
 class QmmError(ValueError):
@@ -263,3 +265,26 @@ def i8t2_gemm(x, W_tile, N, out=None):
     y = out if out is not None else torch.empty((M, N), dtype=torch.int32, device=x.device)
     qmm_i8t2_gemm(x, W_tile, y, M, N, K)
     return y
+
+
+# ------------------------------------------------ round-to-nearest quantizer
+def qmm_quantize(W, w_dtype, qw, scales, qzeros, N, K, w_bit, group_size, symmetric, stream=None):
+    _check(_lib.qmm_quantize(_ptr(W), w_dtype, _ptr(qw), _ptr(scales), _ptr(qzeros), N, K, w_bit,
+                             group_size, int(symmetric), _stream(stream)))
+
+
+def quantize(W, w_bit, group_size, symmetric=False):
+    """W (K, N) float32 / float16 / bfloat16 -> (qw, scales, qzeros or None),
+    the canonical operands of gemv / pack + gemm."""
+    K, N = W.shape
+    codes = {torch.float32: QMM_F32, torch.float16: QMM_F16, torch.bfloat16: QMM_BF16}
+    if W.dtype not in codes:
+        raise QmmError(QMM_ERR_ARG, f"W must be float32, float16 or bfloat16, got {W.dtype}")
+    pack = 32 // w_bit
+    G = 1 if group_size == QMM_PER_COLUMN else K // max(group_size, 1)
+    qw = torch.empty((K // pack, N), dtype=torch.int32, device=W.device)
+    sc = torch.empty((G, N), dtype=torch.float16, device=W.device)
+    qz = None if symmetric else torch.empty(((G + pack - 1) // pack, N), dtype=torch.int32,
+                                            device=W.device)
+    qmm_quantize(W, codes[W.dtype], qw, sc, qz, N, K, w_bit, group_size, symmetric)
+    return qw, sc, qz

@@ -358,4 +358,28 @@ qmm_status qmm_i8t2_gemm(const void* x, const void* W_tile, int32_t* y, int M, i
                                                  reinterpret_cast<hipStream_t>(stream)));
 }
 
+qmm_status qmm_quantize(const void* W, int w_dtype, void* qw, void* scales, void* qzeros, int N,
+                        int K, int w_bit, int group_size, int symmetric, void* stream) {
+  const char* fn = "qmm_quantize";
+  if (w_dtype != QMM_F32 && w_dtype != QMM_F16 && w_dtype != QMM_BF16)
+    return fail(QMM_ERR_ARG, "%s: w_dtype must be QMM_F32, QMM_F16 or QMM_BF16 (got %d)", fn,
+                w_dtype);
+  if (w_bit == 8) return fail(QMM_ERR_ARG, "%s: w_bit must be 2 or 4 (got 8)", fn);
+  if (symmetric != 0 && symmetric != 1)
+    return fail(QMM_ERR_ARG, "%s: symmetric must be 0 or 1 (got %d)", fn, symmetric);
+  if (symmetric && qzeros != nullptr)
+    return fail(QMM_ERR_ARG, "%s: symmetric quantization writes no zero points (qzeros must be "
+                "NULL)", fn);
+  bool noop = false;
+  // the operand checks of the matmul (sizes, w_bit, group_size, alignment)
+  qmm_status st = check_operands(fn, qw, scales, qzeros, N, K, w_bit, group_size, &noop);
+  if (st != QMM_OK || noop) return noop ? ok() : st;
+  if (W == nullptr || (!symmetric && qzeros == nullptr))
+    return fail(QMM_ERR_ARG, "%s: NULL W%s", fn, symmetric ? "" : " or qzeros");
+  if (!aligned16(W)) return fail(QMM_ERR_ARG, "%s: W must be 16-byte aligned", fn);
+  return device_status(fn, qmm::launch_quantize(W, w_dtype, qw, scales, qzeros, N, K, w_bit,
+                                                gemv_group(K, group_size), symmetric,
+                                                reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -69,6 +69,10 @@ hipError_t launch_t2_unpack(const void* Wt, void* Wp, int N, int K, hipStream_t 
 hipError_t launch_i8t2_gemm(const void* x, const void* Wt, int32_t* y, int M, int N, int K,
                             hipStream_t s);
 
+// ---- round-to-nearest quantizer (quantize.hip) -----------------------------
+hipError_t launch_quantize(const void* W, int w_dtype, void* qw, void* scales, void* qzeros,
+                           int N, int K, int w_bit, int group_size, int symmetric, hipStream_t s);
+
 // Optional integer override from the environment (tile sweeps); -1 if unset.
 int env_int(const char* name);
 

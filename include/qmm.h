@@ -200,6 +200,26 @@ QMM_API qmm_status qmm_t2_unpack_layout(const void* W_tile, void* W_page, int N,
 QMM_API qmm_status qmm_i8t2_gemm(const void* x, const void* W_tile, int32_t* y, int M, int N,
                                  int K, void* stream);
 
+/*
+ * qmm_quantize: the step before the matmul -- round-to-nearest quantization
+ * of W (K, N) (w_dtype QMM_F32, QMM_F16 or QMM_BF16) into the canonical
+ * operands above: qw (K/pack, N) int32, scales (G, N) fp16, and qzeros
+ * (ceil(G/pack), N) int32 (asymmetric; must be NULL when symmetric != 0).
+ * The pages give only those operand shapes (BitDistiller
+ * quant_matmul_kernel); the rule is this library's: per group and column,
+ * over [min(0, min w), max(0, max w)],
+ *   asymmetric: s = (max - min) / (2^b - 1), z = clamp(rint(-min/s), 0, 2^b - 1)
+ *   symmetric:  s = max(|max|, |min|) / (2^(b-1) - 1), z = 2^(b-1)
+ *   q = clamp(rint(w / s) + z, 0, 2^b - 1),
+ * s stored as fp16 (nearest even; 1.0 if that is 0), the codes taken from
+ * the stored scale, every step in fp32 with correctly rounded division and
+ * ties-to-even rint.  w_bit 2 or 4; group_size as for the matmul (including
+ * QMM_PER_COLUMN).
+ */
+QMM_API qmm_status qmm_quantize(const void* W, int w_dtype, void* qw, void* scales, void* qzeros,
+                                int N, int K, int w_bit, int group_size, int symmetric,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

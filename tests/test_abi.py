@@ -23,7 +23,7 @@ def declared():
 
 def test_exports_every_declared_symbol():
     names = declared()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     lib = ctypes.CDLL(qmm.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -162,6 +162,20 @@ def test_ternary_calls_reject():
     assert L.qmm_i8t2_gemm(A, A, MIS, 4, 64, 256, 0) == E_ARG
     assert L.qmm_i8t2_gemm(A, A, A, 4, 64, 320, 0) == E_UNS
     assert L.qmm_i8t2_gemm(None, None, None, 0, 64, 256, 0) == qmm.QMM_OK   # M = 0
+
+
+def test_quantize_rejects():
+    L = qmm._lib
+    assert L.qmm_quantize(A, 9, A, A, A, 64, 128, 4, 128, 0, 0) == E_ARG
+    assert "w_dtype" in qmm.qmm_last_error()
+    assert L.qmm_quantize(A, qmm.QMM_F32, A, A, A, 64, 128, 8, 0, 0, 0) == E_ARG
+    assert L.qmm_quantize(A, qmm.QMM_F32, A, A, A, 64, 128, 4, 128, 1, 0) == E_ARG
+    assert "NULL" in qmm.qmm_last_error()
+    assert L.qmm_quantize(A, qmm.QMM_F32, A, A, None, 64, 128, 4, 128, 0, 0) == E_ARG
+    assert L.qmm_quantize(A, qmm.QMM_F32, A, A, A, 64, 192, 4, 128, 0, 0) == E_ARG  # K % g
+    assert L.qmm_quantize(A, qmm.QMM_F32, A, A, A, 64, 40, 4, -1, 0, 0) == E_UNS    # K % 32
+    assert L.qmm_quantize(None, qmm.QMM_F32, A, A, A, 64, 128, 4, 128, 0, 0) == E_ARG
+    assert L.qmm_quantize(A, qmm.QMM_F16, A, A, None, 0, 128, 4, 128, 1, 0) == qmm.QMM_OK
 
 
 def test_layout_calls_reject():
