@@ -12,76 +12,123 @@
 // correctly rounded division and ties-to-even rint, so the codes are a
 // deterministic function of the inputs.
 //
-// One thread per (zero-word row, column): it walks the `pack` groups that
-// share a zero word, so every output word has one writer; a wave's 64
-// columns make every load and store a contiguous row segment.
+// Two kernels.  rtn_scales_kernel: a workgroup owns one zero-word row (the
+// `pack` groups that share a zero word) for 64 columns; wave w takes the
+// range of group pack * row + w, one column per lane, so every load of a
+// wave is one contiguous 64-column row segment; it stores the fp16 scale,
+// and the waves' zero fields meet in LDS, where wave 0 assembles each zero
+// word (one writer per word).  rtn_codes_kernel: one lane per packed word
+// (pack consecutive k of one column) -- far more lanes in flight than one
+// per group -- reading the scale and zero just stored.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "qmm_device.h"
 #include "qmm_internal.h"
 
 namespace qmm {
 
-template <int W_BIT>
-__global__ __launch_bounds__(256) void rtn_quantize_kernel(const void* __restrict__ W, int w_dtype,
-                                                           uint32_t* __restrict__ qw,
-                                                           uint16_t* __restrict__ sc,
-                                                           uint32_t* __restrict__ qz, int N, int K,
-                                                           int gs, int symmetric) {
+// The input type is a template parameter: with a run-time switch inside the
+// load, every load sat in its own branch and waited for itself.
+template <int WDT> __device__ __forceinline__ float load_w(const void* W, size_t i) {
+  if constexpr (WDT == YF32) return reinterpret_cast<const float*>(W)[i];
+  if constexpr (WDT == XF16) return (float)reinterpret_cast<const _Float16*>(W)[i];
+  if constexpr (WDT == XBF16) return (float)reinterpret_cast<const __bf16*>(W)[i];
+}
+
+template <int W_BIT, int WDT>
+__global__ __launch_bounds__(64 * (32 / W_BIT)) void rtn_scales_kernel(
+    const void* __restrict__ W, uint16_t* __restrict__ sc, uint32_t* __restrict__ qz, int N,
+    int K, int gs, int symmetric) {
   constexpr int PACK = 32 / W_BIT;
   constexpr float QMAX = (float)((1 << W_BIT) - 1);
-  const int G = K / gs;
-  const int ZR = (G + PACK - 1) / PACK;
-  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= (size_t)ZR * N) return;
-  const int zr = (int)(t / N), n = (int)(t % N);
-  auto load = [&](int k) -> float {
-    const size_t i = (size_t)k * N + n;
-    if (w_dtype == YF32) return reinterpret_cast<const float*>(W)[i];
-    if (w_dtype == XF16) return (float)reinterpret_cast<const _Float16*>(W)[i];
-    return (float)reinterpret_cast<const __bf16*>(W)[i];
-  };
+  __shared__ uint32_t zfield[PACK][64];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cblocks = (int)(((unsigned)N + 63u) / 64u);
+  const int zr = (int)(blockIdx.x / cblocks);
+  const int n = (int)(blockIdx.x % cblocks) * 64 + lane;
+  const int g = zr * PACK + wv;
 
-  uint32_t zword = 0;
-  const int g1 = min(G, zr * PACK + PACK);
-  for (int g = zr * PACK; g < g1; ++g) {
+  uint32_t zbits = 0;
+  if (g < K / gs && n < N) {
     float mn = 0.0f, mx = 0.0f;
+#pragma unroll 32
     for (int i = 0; i < gs; ++i) {
-      const float v = load(g * gs + i);
-      if (v < mn) mn = v;
-      if (v > mx) mx = v;
+      const float v = load_w<WDT>(W, (size_t)(g * gs + i) * N + n);
+      mn = fminf(mn, v);
+      mx = fmaxf(mx, v);
     }
-    float s32;
-    if (symmetric) {
-      const float amax = fabsf(mx) > fabsf(mn) ? fabsf(mx) : fabsf(mn);
-      s32 = __fdiv_rn(amax, (float)((1 << (W_BIT - 1)) - 1));
-    } else {
-      s32 = __fdiv_rn(mx - mn, QMAX);
-    }
+    const float s32 = symmetric
+                          ? __fdiv_rn(fmaxf(fabsf(mx), fabsf(mn)), (float)((1 << (W_BIT - 1)) - 1))
+                          : __fdiv_rn(mx - mn, QMAX);
     uint16_t sb = __builtin_bit_cast(uint16_t, (_Float16)s32);
     if ((sb & 0x7FFFu) == 0) sb = 0x3C00u;  // 1.0
     sc[(size_t)g * N + n] = sb;
-    const float s = (float)__builtin_bit_cast(_Float16, sb);
-    float z;
-    if (symmetric) {
-      z = (float)(1 << (W_BIT - 1));
-    } else {
-      z = __builtin_rintf(__fdiv_rn(-mn, s));
-      z = z < 0.0f ? 0.0f : (z > QMAX ? QMAX : z);
-      zword |= (uint32_t)z << ((g % PACK) * W_BIT);
-    }
-    for (int k0 = g * gs; k0 < (g + 1) * gs; k0 += PACK) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int p = 0; p < PACK; ++p) {
-        float q = __builtin_rintf(__fdiv_rn(load(k0 + p), s)) + z;
-        q = q < 0.0f ? 0.0f : (q > QMAX ? QMAX : q);
-        word |= (uint32_t)q << (p * W_BIT);
-      }
-      qw[(size_t)(k0 / PACK) * N + n] = word;
+    if (!symmetric) {
+      const float s = (float)__builtin_bit_cast(_Float16, sb);
+      const float z = __builtin_amdgcn_fmed3f(__builtin_rintf(__fdiv_rn(-mn, s)), 0.0f, QMAX);
+      zbits = (uint32_t)z << (wv * W_BIT);
     }
   }
-  if (!symmetric) qz[(size_t)zr * N + n] = zword;
+  if (!symmetric) {  // uniform: every wave of the workgroup reaches the barrier
+    zfield[wv][lane] = zbits;
+    __syncthreads();
+    if (wv == 0 && n < N) {
+      uint32_t zw = 0;
+#pragma unroll
+      for (int p = 0; p < PACK; ++p) zw |= zfield[p][lane];
+      qz[(size_t)zr * N + n] = zw;
+    }
+  }
+}
+
+// rint(w / s) with the division correctly rounded, as the definition has it,
+// at the cost of a multiply in almost every case: f = w * fl(1/s) is within
+// |w/s| 2^-22 of fl(w/s) (two roundings of 2^-24 each, and fl(w/s)'s own),
+// so when f is farther than |f| 2^-20 from every half-integer, f and fl(w/s)
+// lie strictly inside the same rounding interval and rint gives the same
+// integer.  A word with any element that close (about 1 in 10^4 for random
+// data, and every exact tie) is redone with the correctly rounded division.
+template <int W_BIT, int WDT>
+__global__ __launch_bounds__(256) void rtn_codes_kernel(const void* __restrict__ W,
+                                                        const uint16_t* __restrict__ sc,
+                                                        const uint32_t* __restrict__ qz,
+                                                        uint32_t* __restrict__ qw, int N, int K,
+                                                        int gs, int symmetric) {
+  constexpr int PACK = 32 / W_BIT;
+  constexpr float QMAX = (float)((1 << W_BIT) - 1);
+  // block = (word row kw, 256-column block); the division is the block's
+  const unsigned cblocks = ((unsigned)N + 255u) / 256u;
+  const int kw = (int)(blockIdx.x / cblocks);
+  const int n = (int)(blockIdx.x % cblocks) * 256 + (int)threadIdx.x;
+  if (n >= N) return;
+  const int g = kw * PACK / gs;
+  const float s = (float)__builtin_bit_cast(_Float16, sc[(size_t)g * N + n]);
+  const float z = symmetric ? (float)(1 << (W_BIT - 1))
+                            : (float)((qz[(size_t)(g / PACK) * N + n] >> ((g % PACK) * W_BIT)) &
+                                      ((1u << W_BIT) - 1));
+  const float r = __fdiv_rn(1.0f, s);
+  float v[PACK], q[PACK];
+  bool near = false;
+#pragma unroll
+  for (int p = 0; p < PACK; ++p) v[p] = load_w<WDT>(W, (size_t)(kw * PACK + p) * N + n);
+#pragma unroll
+  for (int p = 0; p < PACK; ++p) {
+    const float f = v[p] * r;
+    q[p] = __builtin_rintf(f);
+    near |= fabsf(f - __builtin_floorf(f) - 0.5f) <= fabsf(f) * 0x1p-20f;
+  }
+  if (near) {
+#pragma unroll
+    for (int p = 0; p < PACK; ++p) q[p] = __builtin_rintf(__fdiv_rn(v[p], s));
+  }
+  uint32_t word = 0;
+#pragma unroll
+  for (int p = 0; p < PACK; ++p)
+    word |= (uint32_t)__builtin_amdgcn_fmed3f(q[p] + z, 0.0f, QMAX) << (p * W_BIT);
+  qw[(size_t)kw * N + n] = word;
 }
 
 hipError_t launch_quantize(const void* W, int w_dtype, void* qw, void* scales, void* qzeros,
@@ -89,17 +136,26 @@ hipError_t launch_quantize(const void* W, int w_dtype, void* qw, void* scales, v
                            hipStream_t st) {
   const int pack = 32 / w_bit;
   const int G = K / group_size, ZR = (G + pack - 1) / pack;
-  const size_t threads = (size_t)ZR * N;
-  const dim3 grid((unsigned)((threads + 255) / 256));
+  const size_t blocks1 = (size_t)ZR * (((size_t)N + 63) / 64);
+  const size_t blocks2 = (size_t)(K / pack) * (((size_t)N + 255) / 256);
+  if (blocks1 > 0x7FFFFFFFu || blocks2 > 0x7FFFFFFFu) return hipErrorInvalidValue;
   auto* q = reinterpret_cast<uint32_t*>(qw);
   auto* s = reinterpret_cast<uint16_t*>(scales);
   auto* z = reinterpret_cast<uint32_t*>(qzeros);
-  if (w_bit == 4)
-    hipLaunchKernelGGL(rtn_quantize_kernel<4>, grid, dim3(256), 0, st, W, w_dtype, q, s, z, N, K,
-                       group_size, symmetric);
-  else
-    hipLaunchKernelGGL(rtn_quantize_kernel<2>, grid, dim3(256), 0, st, W, w_dtype, q, s, z, N, K,
-                       group_size, symmetric);
+  auto go = [&](auto bits, auto wdt) {
+    constexpr int B = decltype(bits)::value, D = decltype(wdt)::value;
+    hipLaunchKernelGGL((rtn_scales_kernel<B, D>), dim3((unsigned)blocks1), dim3(64 * (32 / B)), 0,
+                       st, W, s, z, N, K, group_size, symmetric);
+    hipLaunchKernelGGL((rtn_codes_kernel<B, D>), dim3((unsigned)blocks2), dim3(256), 0, st, W, s,
+                       z, q, N, K, group_size, symmetric);
+  };
+  auto by_dtype = [&](auto bits) {
+    if (w_dtype == YF32) go(bits, std::integral_constant<int, YF32>{});
+    else if (w_dtype == XF16) go(bits, std::integral_constant<int, XF16>{});
+    else go(bits, std::integral_constant<int, XBF16>{});
+  };
+  if (w_bit == 4) by_dtype(std::integral_constant<int, 4>{});
+  else by_dtype(std::integral_constant<int, 2>{});
   return hipGetLastError();
 }
 

@@ -73,3 +73,25 @@ def test_quantize_then_gemv(sym):
 def test_quantize_full_size():
     K = N = 4096
     check(weights(K, N, "f16", seed=4096), K, N, 4, 128, False)
+
+
+@pytest.mark.parametrize("sym,w_bit", [(False, 4), (True, 4), (False, 2)])
+def test_quantize_ties_bit_exact(sym, w_bit):
+    """Groups whose scale is exactly 2^-6, filled with weights at exact
+    half-integer multiples of it (ties, rounded to even) and one ulp to
+    either side of them: every rounding decision sits on a boundary."""
+    K, N, gs = 256, 64, 32
+    qmax = (1 << w_bit) - 1
+    lo, hi = (-(1 << (w_bit - 1)) + 1, (1 << (w_bit - 1)) - 1) if sym else (0, qmax)
+    rng = np.random.default_rng(w_bit + 2 * sym)
+    step = np.float32(2.0 ** -6)
+    k = rng.integers(lo, hi, (K, N)).astype(np.float32)           # ties between k and k + 1
+    W = (k + np.float32(0.5)) * step
+    nudge = rng.integers(-1, 2, (K, N))                              # -1, 0, +1 ulp
+    W = np.where(nudge < 0, np.nextafter(W, np.float32(-1)),
+                 np.where(nudge > 0, np.nextafter(W, np.float32(1)), W)).astype(np.float32)
+    W[0::gs] = lo * step                                             # range fixes s = 2^-6
+    W[1::gs] = hi * step
+    check(torch.from_numpy(W), K, N, w_bit, gs, sym)
+    _, sc, _ = oracle.rtn_quantize(W, N, K, w_bit, gs, sym)
+    assert np.all(sc == 0x2400)                                      # 2^-6 in fp16
