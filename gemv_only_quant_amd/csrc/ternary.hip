@@ -85,6 +85,15 @@ __device__ __forceinline__ u32x4_t t2_operand(uint32_t w) {
   return b;
 }
 
+// int8 MFMA whose accumulator is pinned to the matrix-core (AGPR) registers:
+// with the builtin, the allocator splits the GEMM's MT x NT4 accumulators
+// between the two register files and moves them back and forth every stage.
+// Every accumulator is used once per MT x NT4 MFMAs, far beyond the result
+// latency, so the loop needs no extra wait states.
+__device__ __forceinline__ void mfma_i8_acc(i32x4_t& c, const u32x4_t& a, const u32x4_t& b) {
+  asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+}
+
 // Workgroup tile 16 MT rows x 64 NT4 columns: 4 waves side by side along N,
 // each NT4 strips of 16 columns, MT 16-row tiles; 256-deep stages.
 template <int MT, int NT4>
@@ -150,18 +159,26 @@ __global__ __launch_bounds__(256) void i8t2_gemm_kernel(const int8_t* __restrict
     load_w(stn, fill);
     load_x(stn, buf ^ 1);
     __builtin_amdgcn_sched_barrier(0);
+    // A fragments are read from LDS two row tiles ahead of their MFMAs, in
+    // consumption order (k step major, row tile minor), so the LDS latency
+    // overlaps the MFMAs of the tiles in between
     const u32x4_t* xs = &xa[buf][0];
+    constexpr int NF = MT * STEPS;
+    auto frag = [&](int c) { return xs[((c % MT) * STEPS + c / MT) * 64 + lane]; };
+    u32x4_t ar[3];
+    ar[0] = frag(0);
+    if (NF > 1) ar[1] = frag(1);
 #pragma unroll
     for (int j = 0; j < STEPS; ++j) {
       u32x4_t bn[NT4];
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        const u32x4_t a = xs[(i * STEPS + j) * 64 + lane];
+        const int c = j * MT + i;
+        if (c + 2 < NF) ar[(c + 2) % 3] = frag(c + 2);
+        const u32x4_t a = ar[c % 3];
 #pragma unroll
         for (int s = 0; s < NT4; ++s)
-          acc[i][s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a),
-                                                            __builtin_bit_cast(i32x4_t, b[s]),
-                                                            acc[i][s], 0, 0, 0);
+          mfma_i8_acc(acc[i][s], a, b[s]);
         // next k step's operands, spread over the row tiles
         if (j + 1 < STEPS) {
 #pragma unroll
@@ -187,6 +204,16 @@ __global__ __launch_bounds__(256) void i8t2_gemm_kernel(const int8_t* __restrict
     stage(st, wa, wb);
     if (st + 1 < nkb) stage(st + 1, wb, wa);
   }
+  // the accumulators were last written by MFMAs the compiler does not see as
+  // such: give them their result latency, then pass each through an empty asm
+  // ordered after that, so no read of one moves above it
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int s = 0; s < NT4; ++s) asm volatile("" : "+a"(acc[i][s]));
+  __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
   for (int s = 0; s < NT4; ++s) {
