@@ -6,7 +6,7 @@ the current stream.  Functions carry the C names; a non-OK status raises
 ``QmmError`` (a ValueError) with the library's message.
 
 There is no fallback: importing this package without a built libqmm.so
-raises ImportError.  Build it with ``python -m gemv_only_quant_amd.build``.
+raises ImportError.  Build it with ``python gemv_only_quant_amd/build.py``.
 """
 import ctypes
 import os
@@ -22,7 +22,7 @@ QMM_PER_COLUMN = -1  # group_size for per-column scales (one group spanning K)
 QMM_LAYOUT_CANON, QMM_LAYOUT_MFMA = 0, 1
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run python -m gemv_only_quant_amd.build")
+    raise ImportError(f"{LIB_PATH} is not built; run python gemv_only_quant_amd/build.py")
 
 _lib = ctypes.CDLL(LIB_PATH)
 _P, _I, _S = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
