@@ -104,7 +104,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
   constexpr uint32_t ZSYM = W_BIT == 4 ? 0x88888888u : 0xAAAAAAAAu;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index in an SGPR: the per-wave K range and the stage loop are then
+  // scalar (threadIdx.x >> 6 alone is taken as divergent, and the loop would
+  // run under an exec mask with its ring registers reused as temporaries)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, quad = lane >> 4;
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int nt = w % n_tiles, mt_idx = w / n_tiles;
@@ -118,13 +121,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
   const int st0 = min(nst, wave * per);
   const int st1 = min(nst, st0 + per);
 
-  int sidx[NT];
-#pragma unroll
-  for (int s = 0; s < NT; ++s) sidx[s] = min(s0 + s, strips - 1);  // loads stay in bounds
-  int xrow[MT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i) xrow[i] = min(m0 + 16 * i + l16, M - 1);
-
   // One stage in registers: weight slots, x operand fragments, and the
   // scales / zero words of the groups the stage touches.
   struct StageRegs {
@@ -133,33 +129,52 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     uint32_t sc[NT][NGS];
     uint32_t zw[NT];
   };
+  // Stage loads are buffer loads through descriptors based at this
+  // workgroup's strips, rows and columns: offsets stay 32-bit for any
+  // problem size, and a strip or row past the edge reads zeros (the
+  // hardware range check) instead of needing a clamped index.  They are
+  // intrinsic calls, so the compiler keeps each one where it is written: a
+  // plain load that is only used after the loop's back edge gets moved down
+  // to its use, which empties the ring.  Raw values go into the ring; every
+  // conversion happens where the value is used.
+  const int strips_here = min(NT, strips - s0);
+  const int rows_here = min(16 * MT, M - m0);
+  const buf_t qbuf = make_buf(Qt + (size_t)s0 * nblk * 64, (uint32_t)strips_here * nblk * 1024u);
+  const buf_t xbuf = make_buf(x + (size_t)m0 * K, (uint32_t)rows_here * K * 2u);
+  const uint16_t* s16 = reinterpret_cast<const uint16_t*>(scales);
+  const int G = LOWBIT ? K / GS : 1;  // groups (per-column: index masked to 0)
+  const buf_t sbuf = make_buf(s16 + 16 * s0, LOWBIT ? (uint32_t)((size_t)G * N - 16 * s0) * 2u : 0u);
+  const bool zp = qz != nullptr;
+  const int zrows = (G + PACK - 1) / PACK;
+  const buf_t zbuf = make_buf(zp ? qz + 16 * s0 : reinterpret_cast<const uint32_t*>(Qt),
+                              zp ? (uint32_t)((size_t)zrows * N - 16 * s0) * 4u : 0u);
   auto load_stage = [&](int st, StageRegs& R) {
 #pragma unroll
     for (int s = 0; s < NT; ++s)
 #pragma unroll
       for (int b = 0; b < BLK; ++b) {
         const int kb = min(st * BLK + b, nblk - 1);
-        R.w[s][b] = Qt[((size_t)sidx[s] * nblk + kb) * 64 + lane];
+        R.w[s][b] = buf_load128(qbuf, ((s * nblk + kb) * 64 + lane) * 16);
       }
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int k = 0; k < STEPS; ++k) {
-        // int8 stages are two 64-deep blocks: past the last block (odd block
-        // count) x is zero, so that half adds nothing
-        const int col = st * KS + 32 * k + 8 * quad;
-        R.a[i][k] = col < K ? *reinterpret_cast<const u32x4_t*>(x + (size_t)xrow[i] * K + col)
-                            : u32x4_t{0u, 0u, 0u, 0u};
+        // int8 stages are two 64-deep blocks; past the last block (odd block
+        // count) the column is clamped here and the k steps are skipped
+        const int col = LOWBIT ? st * KS + 32 * k + 8 * quad
+                               : min(st * KS + 32 * k, K - 32) + 8 * quad;
+        R.a[i][k] = buf_load128(xbuf, ((16 * i + l16) * K + col) * 2);
       }
     if constexpr (LOWBIT) {
       const int g0 = (st * KS) / GS;
-      const uint16_t* s16 = reinterpret_cast<const uint16_t*>(scales);
 #pragma unroll
       for (int s = 0; s < NT; ++s) {
-        const int n = 16 * sidx[s] + l16;
+        const int nl = 16 * s + l16;  // column within the workgroup's strips
 #pragma unroll
-        for (int q = 0; q < NGS; ++q) R.sc[s][q] = s16[(size_t)((g0 + q) & gmask) * N + n];
-        R.zw[s] = qz != nullptr ? qz[(size_t)((g0 & gmask) / PACK) * N + n] : ZSYM;
+        for (int q = 0; q < NGS; ++q)
+          R.sc[s][q] = buf_load16(sbuf, (((g0 + q) & gmask) * N + nl) * 2);
+        R.zw[s] = buf_load32(zbuf, (((g0 & gmask) / PACK) * N + nl) * 4);
       }
     }
   };
@@ -192,6 +207,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
   auto compute_stage = [&](int st, const StageRegs& R, bool last) {
 #pragma unroll
     for (int k = 0; k < STEPS; ++k) {
+      if (!LOWBIT && st * KS + 32 * k >= K) break;  // int8: half stage past K
 #pragma unroll
       for (int i = 0; i < MT; ++i) xs[i] = mfma16<XDT>(R.a[i][k], ones, xs[i]);
 #pragma unroll
@@ -209,7 +225,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 #pragma unroll
           for (int s = 0; s < NT; ++s) {
             sc[s] = f16_bits_to_f32((uint16_t)R.sc[s][q]);
-            bz[s] = CB + (float)((R.zw[s] >> ((g % PACK) * W_BIT)) & ((1u << W_BIT) - 1u));
+            const uint32_t zw = zp ? R.zw[s] : ZSYM;
+            bz[s] = CB + (float)((zw >> ((g % PACK) * W_BIT)) & ((1u << W_BIT) - 1u));
           }
           flush(sc, bz);
         }
@@ -222,14 +239,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
   if (st0 < st1) {
     StageRegs ring[DEPTH];
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) load_stage(min(st0 + d, st1 - 1), ring[d]);
+    for (int d = 0; d < DEPTH; ++d) {
+      load_stage(min(st0 + d, st1 - 1), ring[d]);
+      // issue order = ring order, as in the loop: the wait at the loop head
+      // then only needs this slot's loads, not the later slots'
+      __builtin_amdgcn_sched_barrier(0);
+    }
     for (int st = st0; st < st1; st += DEPTH) {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) {
-        if (st + d < st1) {
-          compute_stage(st + d, ring[d], st + d == st1 - 1);
-          load_stage(min(st + d + DEPTH, st1 - 1), ring[d]);
-        }
+        if (st + d < st1) compute_stage(st + d, ring[d], st + d == st1 - 1);
+        load_stage(min(st + d + DEPTH, st1 - 1), ring[d]);  // on every path
       }
     }
   }
@@ -237,7 +257,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     float sc[NT], bz[NT];
 #pragma unroll
     for (int s = 0; s < NT; ++s) {
-      sc[s] = reinterpret_cast<const float*>(scales)[16 * sidx[s] + l16];
+      sc[s] = reinterpret_cast<const float*>(scales)[16 * min(s0 + s, strips - 1) + l16];
       bz[s] = CB;
     }
     flush(sc, bz);

@@ -105,6 +105,24 @@ __device__ __forceinline__ float wave_sum(float v) {
 // Work-item remap so that consecutive work ids land on one XCD: the
 // dispatcher deals workgroups round-robin over the 8 XCDs, so block b runs
 // on XCD b % 8.  Used only when the grid is a multiple of 8.
+// Raw buffer loads (no format conversion) through a descriptor whose range
+// is `bytes`: an offset at or past it reads zeros.  Word 3 is the raw-buffer
+// configuration of the CDNA buffer descriptor (32-bit data format, no
+// swizzle, no stride).
+typedef __amdgpu_buffer_rsrc_t buf_t;
+__device__ __forceinline__ buf_t make_buf(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load128(buf_t b, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(b, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load32(buf_t b, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(b, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load16(buf_t b, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(b, off, 0, 0);
+}
+
 __device__ __forceinline__ int xcd_remap(int b, int total) {
   if (total % 8 != 0) return b;
   return (b % 8) * (total / 8) + b / 8;
