@@ -81,28 +81,31 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lowbit_kernel(
 #pragma unroll
     for (int j = 0; j < PER_T; ++j) {
       const int it = threadIdx.x + j * NT;
-      const int m = it / ROWS_P, rr = it % ROWS_P;
-      const bool ok = it < ITEMS && m < M && r_base + rr < rows;
+      const int m = min(it / ROWS_P, M - 1);
+      const int rr = min(r_base + it % ROWS_P, rows - 1);
 #pragma unroll
       for (int v = 0; v < PACK / 8; ++v)
-        xr[j][v] = ok ? *reinterpret_cast<const u32x4_t*>(
-                            x + (size_t)m * K + (size_t)(r_base + rr) * PACK + 8 * v)
-                      : u32x4_t{0u, 0u, 0u, 0u};
+        xr[j][v] = *reinterpret_cast<const u32x4_t*>(x + (size_t)m * K + (size_t)rr * PACK + 8 * v);
     }
 
-    // 2. every weight load of this lane for the pass
+    // 2. every weight load of this lane for the pass.  Loads are never
+    // predicated: a dead lane reads a clamped, valid address and its result
+    // is dropped in step 6.  (Loads under a lane mask leave the compiler
+    // unsure how many loads follow the x slice, and it then waits for all of
+    // them before x can go to LDS.)
+    const int rowc = live ? row0 : 0;
+    const int nc = col_ok ? n0 : 0;
     u32x4_t wq[RL];
 #pragma unroll
     for (int i = 0; i < RL; ++i)
-      wq[i] = live ? *reinterpret_cast<const u32x4_t*>(qw + (size_t)(row0 + i) * N + n0)
-                   : u32x4_t{0u, 0u, 0u, 0u};
+      wq[i] = *reinterpret_cast<const u32x4_t*>(qw + (size_t)(rowc + i) * N + nc);
 
     // 3. scale and zero point of the lane's group, for its four columns
-    const int g = live ? (row0 * PACK) / group_size : 0;
-    uint2 s2 = live ? *reinterpret_cast<const uint2*>(sc + (size_t)g * N + n0) : uint2{0u, 0u};
+    const int g = (rowc * PACK) / group_size;
+    uint2 s2 = *reinterpret_cast<const uint2*>(sc + (size_t)g * N + nc);
     u32x4_t zw = u32x4_t{0u, 0u, 0u, 0u};
-    if (qz != nullptr && live)
-      zw = *reinterpret_cast<const u32x4_t*>(qz + (size_t)(g / PACK) * N + n0);
+    if (qz != nullptr)  // uniform: no lane mask
+      zw = *reinterpret_cast<const u32x4_t*>(qz + (size_t)(g / PACK) * N + nc);
 
     // 4. x to LDS as (x[t], x[t + PAIRS]) pairs
     if (p > 0) __syncthreads();  // previous pass done reading xl
@@ -111,12 +114,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lowbit_kernel(
       const int it = threadIdx.x + j * NT;
       if (it < ITEMS) {
         const int m = it / ROWS_P, rr = it % ROWS_P;
+        const bool ok = m < M && r_base + rr < rows;  // else x is zero
         uint32_t* dst = xl + (m * GROUPS + rr / RL) * GSTRIDE + (rr % RL) * PAIRS;
         uint32_t d[PAIRS];
 #pragma unroll
         for (int v = 0; v < PACK / 8; ++v)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) d[4 * v + e] = xr[j][v][e];
+          for (int e = 0; e < 4; ++e) d[4 * v + e] = ok ? xr[j][v][e] : 0u;
 #pragma unroll
         for (int t = 0; t < PAIRS; ++t) {
           const uint32_t a = d[t / 2], b = d[t / 2 + PAIRS / 2];
