@@ -1,6 +1,7 @@
 """Benchmark of the weight-only quantized matmul on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
+    python bench.py --probe WORKLOAD      (three calls, for rocprofv3 --pmc)
 
 A step is one call of the hot path on one batch of synthetic input already
 resident in HBM.  The headline workload is the int4 group-128 asymmetric
@@ -315,6 +316,39 @@ def line(r, path):
     return out
 
 
+def probe(name):
+    """Counter probe for rocprofv3 --pmc: three calls of one workload's entry
+    point, each on its own copy of the weights (a pool of >= 512 MB, so no
+    call finds its weights in cache), then three copies of a 256 MiB device
+    buffer (kernel __amd_rocclr_copyBuffer), whose counter readings give the
+    scale of known byte counts (256 MiB read, 256 MiB written)."""
+    import torch
+    import gemv_only_quant_amd as qmm
+    import synth_inputs as si
+
+    path = "gemv" if name == HEADLINE or dict(OTHERS).get(name) == "gemv" else "gemm"
+    case = si.workload(name)
+    wbytes, _ = bytes_of(case)
+    d = case.to("cuda")
+    Q0 = d.Q if path == "gemv" else qmm.pack(d.Q, case.N, case.K, case.w_bit)
+    copies = max(3, -(-POOL_BYTES // wbytes))
+    pool = [(Q0.clone(), d.scales.clone(), None if d.zeros is None else d.zeros.clone())
+            for _ in range(copies)]
+    y = torch.empty((case.M, case.N), dtype=torch.float32, device="cuda")
+    fn = qmm.qmm_gemv if path == "gemv" else qmm.qmm_gemm
+    torch.cuda.synchronize()
+    for i in range(3):
+        Q, s, z = pool[(i * copies) // 3]
+        fn(d.x, Q, s, z, y, case.M, case.N, case.K, case.w_bit, case.group_size)
+    torch.cuda.synchronize()
+    src = torch.ones(1 << 27, dtype=torch.int16, device="cuda")  # 256 MiB
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"probe {name}: 3 x qmm_{path} ({copies} weight copies), 3 x 256 MiB copy", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -322,6 +356,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--quick", action="store_true", help="headline only")
+    ap.add_argument("--probe", metavar="WORKLOAD",
+                    help="three calls of one workload and a 256 MiB copy, for counter runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -332,6 +368,9 @@ def main():
     import torch
     import synth_inputs as si
     torch.cuda.set_device(0)
+    if args.probe:
+        probe(args.probe)
+        return
     r = time_workload(HEADLINE, args.steps, args.warmup, "gemv")
     case, us = r["case"], r["us"]
     achieved = r["tbytes"] / (us * 1e-6) / 1e9
