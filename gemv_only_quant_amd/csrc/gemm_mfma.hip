@@ -121,7 +121,25 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
   const int st0 = min(nst, wave * per);
   const int st1 = min(nst, st0 + per);
 
-  // One stage in registers: weight slots, x operand fragments, and the
+  // x of a stage arrives as whole rows (CH 16-byte chunks of a row per
+  // stage, 64 / CH rows per load: a fragment-order load would touch 16 rows
+  // x 64 bytes, which the memory pipeline serves at well under half the
+  // rate) and is turned into A-operand fragments through a per-wave LDS
+  // tile of 16 rows x CH chunks; chunk c of row r sits at slot CH r + (c ^ r),
+  // so both the row-wise writes and the fragment reads (16 rows, one chunk
+  // each) hit 16 distinct bank groups.  A wave's LDS operations run in
+  // order, so the tile needs no barrier between stages.  The reduction of
+  // the waves' partial tiles reuses the same LDS after the K loop.
+  constexpr int CH = KS / 8, RPL = 64 / CH;
+  constexpr int ROWS = 16 * MT, COLS = 16 * NT;
+  constexpr size_t XT_BYTES = (size_t)WAVES * MT * 16 * CH * 16;
+  constexpr size_t RED_BYTES = (size_t)WAVES * ROWS * (COLS + 1) * 4;
+  static_assert(XT_BYTES <= 160 * 1024 && RED_BYTES <= 96 * 1024, "LDS");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[XT_BYTES > RED_BYTES ? XT_BYTES : RED_BYTES];
+  u32x4_t* const xt = reinterpret_cast<u32x4_t*>(smem);
+  auto xswz = [](int r, int c) { return CH * r + (c ^ r); };
+
+  // One stage in registers: weight slots, x rows, and the
   // scales / zero words of the groups the stage touches.
   struct StageRegs {
     u32x4_t w[NT][BLK];
@@ -160,11 +178,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int k = 0; k < STEPS; ++k) {
-        // int8 stages are two 64-deep blocks; past the last block (odd block
-        // count) the column is clamped here and the k steps are skipped
-        const int col = LOWBIT ? st * KS + 32 * k + 8 * quad
-                               : min(st * KS + 32 * k, K - 32) + 8 * quad;
-        R.a[i][k] = buf_load128(xbuf, ((16 * i + l16) * K + col) * 2);
+        // contiguous rows: load k of row tile i is rows RPL k .. RPL k +
+        // RPL - 1, 16-byte chunk lane % CH of each row's stage.  (int8: a
+        // stage past the last 64-deep block reads the next row or zeros into
+        // its upper chunks, which only the skipped k steps would use.)
+        const int row = 16 * i + RPL * k + lane / CH;
+        R.a[i][k] = buf_load128(xbuf, (row * K + st * KS + 8 * (lane % CH)) * 2);
       }
     if constexpr (LOWBIT) {
       const int g0 = (st * KS) / GS;
@@ -205,16 +224,28 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
   };
 
   auto compute_stage = [&](int st, const StageRegs& R, bool last) {
+    // x through the wave's LDS tile: rows in, A-operand fragments out
+    u32x4_t af[MT][STEPS];
+    u32x4_t* xw = xt + (size_t)wave * MT * 16 * CH;
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int k = 0; k < STEPS; ++k)
+        xw[i * 16 * CH + xswz(RPL * k + lane / CH, lane % CH)] = R.a[i][k];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int k = 0; k < STEPS; ++k) af[i][k] = xw[i * 16 * CH + xswz(l16, 4 * k + quad)];
 #pragma unroll
     for (int k = 0; k < STEPS; ++k) {
       if (!LOWBIT && st * KS + 32 * k >= K) break;  // int8: half stage past K
 #pragma unroll
-      for (int i = 0; i < MT; ++i) xs[i] = mfma16<XDT>(R.a[i][k], ones, xs[i]);
+      for (int i = 0; i < MT; ++i) xs[i] = mfma16<XDT>(af[i][k], ones, xs[i]);
 #pragma unroll
       for (int s = 0; s < NT; ++s) {
         const u32x4_t b = bfrag<W_BIT, XDT>(R.w[s], k);
 #pragma unroll
-        for (int i = 0; i < MT; ++i) acc[i][s] = mfma16<XDT>(R.a[i][k], b, acc[i][s]);
+        for (int i = 0; i < MT; ++i) acc[i][s] = mfma16<XDT>(af[i][k], b, acc[i][s]);
       }
       if constexpr (LOWBIT) {
         const int kend = st * KS + 32 * (k + 1);  // one past this step
@@ -263,10 +294,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     flush(sc, bz);
   }
 
-  // ---- the waves' K ranges meet in LDS -----------------------------------
-  constexpr int ROWS = 16 * MT, COLS = 16 * NT;
-  __shared__ float red[WAVES][ROWS][COLS + 1];
-  static_assert(sizeof(red) <= 96 * 1024, "reduction tile too large for this wave count");
+  // ---- the waves' K ranges meet in LDS (over the x tiles: wait for all) ---
+  __syncthreads();
+  float (*red)[ROWS][COLS + 1] = reinterpret_cast<float (*)[ROWS][COLS + 1]>(smem);
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
