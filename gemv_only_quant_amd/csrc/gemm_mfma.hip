@@ -160,7 +160,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
   const buf_t qbuf = make_buf(Qt + (size_t)s0 * nblk * 64, (uint32_t)strips_here * nblk * 1024u);
   const buf_t xbuf = make_buf(x + (size_t)m0 * K, (uint32_t)rows_here * K * 2u);
   const uint16_t* s16 = reinterpret_cast<const uint16_t*>(scales);
-  const int G = LOWBIT ? K / GS : 1;  // groups (per-column: index masked to 0)
+  const int G = LOWBIT && gmask != 0 ? K / GS : 1;  // scale rows (per-column: one)
   const buf_t sbuf = make_buf(s16 + 16 * s0, LOWBIT ? (uint32_t)((size_t)G * N - 16 * s0) * 2u : 0u);
   const bool zp = qz != nullptr;
   const int zrows = (G + PACK - 1) / PACK;

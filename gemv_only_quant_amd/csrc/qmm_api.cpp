@@ -249,6 +249,14 @@ static qmm_status gemm_impl(const char* fn, const void* x, const void* Q, const 
   const int gs = gemm_group(K, group_size);
   const qmm::GemmPlan p = qmm::plan_gemm(M, N, K, w_bit, gs);
   if (p.kind < 0) return fail(QMM_ERR_UNSUPPORTED, "%s: no MFMA kernel for this shape", fn);
+  // the skinny kernel addresses a workgroup's scale and zero rows with 32-bit
+  // byte offsets: the scale table must stay below 2 GiB
+  if (p.kind == 0 && w_bit != 8) {
+    const int64_t G = group_size == QMM_PER_COLUMN ? 1 : K / group_size;
+    if (G * (int64_t)N >= (int64_t(1) << 30))
+      return fail(QMM_ERR_UNSUPPORTED, "%s: scale table of %lld x %d too large (< 2^30 entries)",
+                  fn, (long long)G, N);
+  }
   st = check_workspace(fn, p.workspace_bytes, workspace, workspace_bytes);
   if (st != QMM_OK) return st;
   qmm::MatmulArgs a{x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit, gs, group_mask(group_size),

@@ -111,6 +111,8 @@ GEMM_BAD = [
     (dict(w_bit=2, K=128, group_size=64), E_UNS, "K % 256"),
     (dict(w_bit=8, group_size=0, K=96), E_UNS, "K % 64"),
     (dict(y=MIS), E_ARG, "aligned"),
+    # skinny kernel: 32-bit byte offsets into the scale table (2^14 groups x 2^16 columns)
+    (dict(M=16, N=65536, K=524288, group_size=32), E_UNS, "too large"),
 ]
 
 
