@@ -400,7 +400,9 @@ def main():
         out["workloads"] = [line(time_workload(n, 200, 20, p), p) for n, p in OTHERS]
         pre = []
         for n, out_dt in PREFILL:
-            p = time_workload(n, 10, 3, "gemm", out_dt)
+            # 50 calls (about 20 ms) per replay: 10-call replays (4 ms) measured 416 us per
+            # call against 363 at 50 and 362 at 200 -- too short to reach steady clocks
+            p = time_workload(n, 50, 10, "gemm", out_dt)
             tf = p["flops"] / (p["us"] * 1e-6) / 1e12
             pre.append({"workload": n, "entry": "qmm_gemm" if out_dt == "f32" else "qmm_gemm_ex",
                         "y_dtype": out_dt, "us_per_call": round(p["us"], 2),
@@ -410,7 +412,7 @@ def main():
             if t is not None:
                 pre[-1]["traffic_bytes"] = t
         out["prefill"] = pre
-        out["ternary"] = [time_ternary(n, 200 if n.startswith("i8t2_m16") else 10, 5)
+        out["ternary"] = [time_ternary(n, 200 if n.startswith("i8t2_m16") else 50, 10)
                           for n in TERNARY]
         out["quantize"] = [time_quantize(4096, 4096, 4, 128)]
         out["calibration"] = calibration()
