@@ -251,7 +251,16 @@ __global__ __launch_bounds__(256) void i8t2_skinny_kernel(const int8_t* __restri
   for (int s = 0; s < NT; ++s) sidx[s] = min(s0 + s, strips - 1);
   const int per = (nkb + 3) / 4;
   const int kb0 = min(nkb, wave * per), kb1 = min(nkb, kb0 + per);
-  const int8_t* xrow = x + (size_t)min(m0 + l16, M - 1) * K + 16 * quad;
+  // x arrives as whole rows (load j: rows 4j .. 4j + 3, 16-byte chunk l16 of
+  // each row's 256-byte block) and becomes A fragments through a per-wave
+  // LDS tile, chunk c of row r at slot 16 r + (c ^ r) (conflict-free both
+  // ways; a wave's LDS operations run in order, so no barrier): an
+  // operand-order load would touch 16 rows x 64 bytes, a slow pattern.
+  __shared__ u32x4_t xt[4][256];
+  u32x4_t* const xw = xt[wave];
+  const int8_t* xrows[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) xrows[j] = x + (size_t)min(m0 + 4 * j + quad, M - 1) * K + 16 * l16;
 
   i32x4_t acc[NT];
 #pragma unroll
@@ -265,17 +274,22 @@ __global__ __launch_bounds__(256) void i8t2_skinny_kernel(const int8_t* __restri
       for (int s = 0; s < NT; ++s) wr[d][s] = Wt[((size_t)sidx[s] * nkb + k) * 64 + lane];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        xr[d][j] = *reinterpret_cast<const u32x4_t*>(xrow + (size_t)k * 256 + 64 * j);
+        xr[d][j] = *reinterpret_cast<const u32x4_t*>(xrows[j] + (size_t)k * 256);
     }
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       if (kb + d < kb1) {
+        u32x4_t af[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xw[16 * (4 * j + quad) + (l16 ^ (4 * j + quad))] = xr[d][j];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) af[j] = xw[16 * l16 + ((4 * j + quad) ^ l16)];
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int s = 0; s < NT; ++s)
             acc[s] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
-                __builtin_bit_cast(i32x4_t, xr[d][j]),
+                __builtin_bit_cast(i32x4_t, af[j]),
                 __builtin_bit_cast(i32x4_t, t2_operand(wr[d][s][j])), acc[s], 0, 0, 0);
       }
     }
