@@ -419,12 +419,31 @@ static constexpr int kWaitVm0 = 0x0F70;
 struct GroupConst {
   float s;          // scale
   float zb_s;       // (1024 + z) * s
+  float s16;        // s / 16            (int4 bf16: odd fields, read as 1024 + 16 q)
+  float zb16_s;     // (64 + z) * s
   uint32_t s_h2;    // scale as an fp16 pair
   uint32_t nzb_h2;  // -(1024 + z) as an fp16 pair
 };
 
 template <int W_BIT, int XDT>
 __device__ __forceinline__ uint32_t bpair_scaled(uint32_t w, int h, int t, const GroupConst& g) {
+  if constexpr (W_BIT == 4 && XDT == XBF16) {
+    // Fields t = 1, 3 are taken where they sit, at bits 4-7 of each half:
+    // OR-ed under the fp16 1024 pattern they read 1024 + 16 q, and
+    // (1024 + 16 q) * s / 16 - (64 + z) * s = (q - z) * s, still exact in
+    // fp32 (11-bit by 11-bit products, power-of-two scaling).  One shift
+    // by 8 serves fields 2 and 3, so a word costs one shift and four
+    // mask-ors instead of three shifts.  Same bits out as the plain path.
+    const uint32_t v = t >= 2 ? w >> 8 : w;
+    const uint32_t m = (v & ((t & 1) ? 0x00F000F0u : 0x000F000Fu)) | 0x64006400u;
+    const half2_t mh = __builtin_bit_cast(half2_t, m);
+    const float sc = (t & 1) ? g.s16 : g.s;
+    const float zb = (t & 1) ? g.zb16_s : g.zb_s;
+    const float lo = __builtin_fmaf((float)mh[0], sc, -zb);
+    const float hi = __builtin_fmaf((float)mh[1], sc, -zb);
+    bf16x2_t r = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, r);
+  }
   constexpr uint32_t FIELD2 = W_BIT == 4 ? 0x000F000Fu : 0x00030003u;
   const int sh = W_BIT == 4 ? 4 * t : 2 * (4 * h + t);
   const uint32_t m = ((w >> sh) & FIELD2) | 0x64006400u;
@@ -560,6 +579,8 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
       const float zb = 1024.0f + (float)z;
       g[q].s = sc;
       g[q].zb_s = zb * sc;
+      g[q].s16 = sc * 0.0625f;
+      g[q].zb16_s = (64.0f + (float)z) * sc;
       g[q].s_h2 = sb | (sb << 16);
       const uint32_t nzb = __builtin_bit_cast(uint16_t, (_Float16)(-zb));
       g[q].nzb_h2 = nzb | (nzb << 16);
