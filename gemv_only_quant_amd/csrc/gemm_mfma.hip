@@ -8,8 +8,9 @@
 //  * per stage (128 k; 256 k for int2; two 64-deep blocks for int8) a lane
 //    loads ONE 16-byte slot of each strip's 1 KiB layout block -- already
 //    the MFMA B-operand lane map -- so weights go HBM -> VGPR -> MFMA
-//    without LDS, and its x operand fragments straight from global memory;
-//    a DEPTH-deep ring of stages in registers keeps the loads in flight;
+//    without LDS; x arrives as whole rows and becomes operand fragments
+//    through a small per-wave LDS tile; a DEPTH-deep ring of stages in
+//    registers (buffer loads, issued in ring order) keeps the loads in flight;
 //  * codes become operand pairs (B + q_a, B + q_b) with one mask-or per pair
 //    (fp16 B = 1024, bf16 B = 128; int8: u = q + 128 through a byte perm
 //    (fp16) or byte->float->bf16 converts (bf16)), exact in 16 bits;

@@ -231,8 +231,9 @@ __global__ __launch_bounds__(256) void i8t2_gemm_kernel(const int8_t* __restrict
 
 // Decode-sized M (one 16-row tile): a workgroup owns NT strips, and its 4
 // waves split K into quarters (as the skinny low-bit GEMM does), each with
-// up to 4 stages of weight slots and x fragments in flight straight to
-// registers; the 4 partial tiles meet in LDS.
+// up to 4 stages of weight slots and x rows in flight straight to
+// registers (x then passes through a per-wave LDS tile into operand
+// order); the 4 partial tiles meet in LDS.
 template <int NT>
 __global__ __launch_bounds__(256) void i8t2_skinny_kernel(const int8_t* __restrict__ x,
                                                           const u32x4_t* __restrict__ Wt,
