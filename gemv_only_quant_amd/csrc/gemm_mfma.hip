@@ -496,23 +496,31 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
 #pragma unroll
   for (int s = 0; s < NT; ++s) sidx[s] = min(s0 + s, strips - 1);
 
-  // x fragment f of a stage (row tile f / STEPS, k step f % STEPS) is one
-  // 1 KiB block in A-operand lane order: lane p holds row 16 (f / STEPS) +
-  // p % 16, k 32 (f % STEPS) + 8 (p / 16) .. + 7.  Each wave moves its
-  // FRAGS / 4 fragments straight from global memory into LDS (lane p's 16
-  // bytes land at block + 16 p).  Rows past M read row M - 1 instead: they
-  // only feed output rows that are never stored.
+  // The x tile of a stage is stored by row tile: 16 rows x 16 chunks of 16
+  // bytes (the stage's 128 k of a row), chunk c of row r at slot 16 r +
+  // (c ^ r).  Load unit f (1 KiB, row tile f / 4) fills slots 64 (f % 4) ..
+  // + 63 of its tile: lane p's 16 bytes land at slot 64 (f % 4) + p, i.e.
+  // row r = 4 (f % 4) + p / 16, position p % 16 -- so lane p fetches chunk
+  // (p % 16) ^ r of that row, and one load reads 4 whole rows (256
+  // contiguous bytes each; the fragment-order alternative, 16 rows x 64
+  // bytes per load, is served at well under half the rate).  A fragment
+  // (row l16, chunk 4 kk + quad) is then one conflict-free ds_read_b128.
+  // Each wave moves FRAGS / 4 units straight from global memory into LDS.
+  // Rows past M read row M - 1 instead: they only feed output rows that are
+  // never stored.
+  static_assert(KS == 128 && STEPS == 4, "x tile layout: 16 chunks per row, 4 loads per row tile");
   const int rows_left = M - 1 - m0;
+  auto x_unit = [&](int f, int sx, int buf) {
+    const int r = 4 * (f % 4) + quad;
+    const int rr = min(16 * (f / 4) + r, rows_left);
+    const int k = sx * KS + 8 * (l16 ^ r);
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(x + (size_t)(m0 + rr) * K + k),
+        (__attribute__((address_space(3))) void*)(&xa[buf][f * 64]), 16, 0, 0);
+  };
   auto load_x = [&](int st, int buf) {
 #pragma unroll
-    for (int j = 0; j < FRAGS / 4; ++j) {
-      const int f = wave * (FRAGS / 4) + j;
-      const int rr = min(16 * (f / STEPS) + l16, rows_left);
-      const int k = st * KS + 32 * (f % STEPS) + 8 * quad;
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(x + (size_t)(m0 + rr) * K + k),
-          (__attribute__((address_space(3))) void*)(&xa[buf][f * 64]), 16, 0, 0);
-    }
+    for (int j = 0; j < FRAGS / 4; ++j) x_unit(wave * (FRAGS / 4) + j, st, buf);
   };
 
   struct WRegs {
@@ -553,12 +561,7 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
       if constexpr (ZP) R.zw[s] = qz[(size_t)((g0 & gmask) / PACK) * N + 16 * sidx[s] + l16];
       else R.zw[s] = ZSYM;
     } else {
-      const int f = wave * (FRAGS / 4) + (j - NWL);
-      const int rr = min(16 * (f / STEPS) + l16, rows_left);
-      const int k = sx * KS + 32 * (f % STEPS) + 8 * quad;
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(x + (size_t)(m0 + rr) * K + k),
-          (__attribute__((address_space(3))) void*)(&xa[buf][f * 64]), 16, 0, 0);
+      x_unit(wave * (FRAGS / 4) + (j - NWL), sx, buf);
     }
   };
 
@@ -647,8 +650,10 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
     // group constants -- and (3) part of the next stage's loads is issued.
     // The scheduling barriers hold this interleave; without them the
     // compiler hoists every read and every conversion (and spills).
-    u32x4_t a0 = xs_buf[(0 * STEPS + 0) * 64 + lane];
-    u32x4_t a1 = xs_buf[(1 * STEPS + 0) * 64 + lane];
+    // fragment (row tile i, k step kk) = slot 256 i + 16 l16 + ((4 kk + quad) ^ l16)
+    auto afrag = [&](int i, int kk) { return xs_buf[256 * i + 16 * l16 + ((4 * kk + quad) ^ l16)]; };
+    u32x4_t a0 = afrag(0, 0);
+    u32x4_t a1 = afrag(1, 0);
 #pragma unroll
     for (int k = 0; k < STEPS; ++k) {
       const int kn = k + 1;
@@ -657,7 +662,7 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
       for (int i = 0; i < MT; ++i) {
         const int t2 = k * MT + i + 2;  // fragment two ahead, in (k, i) order
         u32x4_t an = a1;
-        if (t2 < STEPS * MT) an = xs_buf[((t2 % MT) * STEPS + t2 / MT) * 64 + lane];
+        if (t2 < STEPS * MT) an = afrag(t2 % MT, t2 / MT);
 #pragma unroll
         for (int s = 0; s < NT; ++s) mfma16_acc<XDT>(acc[i][s], a0, b[s]);
         if (kn < STEPS) {
