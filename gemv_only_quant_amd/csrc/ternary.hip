@@ -119,15 +119,23 @@ __global__ __launch_bounds__(256) void i8t2_gemm_kernel(const int8_t* __restrict
   for (int s = 0; s < NT4; ++s) sidx[s] = min(s0 + s, strips - 1);  // loads stay in bounds
   const int rows_left = M - 1 - m0;
 
-  // x fragment f (row tile f / STEPS, k step f % STEPS): lane p holds row
-  // 16 (f / STEPS) + p % 16, bytes k = 64 (f % STEPS) + 16 (p / 16) .. + 15;
-  // rows past M read row M - 1 (never stored)
+  // The x tile of a stage is stored by row tile: 16 rows x 16 chunks of 16
+  // bytes (the stage's 256 k of a row), chunk c of row r at slot 16 r +
+  // (c ^ r).  Load unit f (1 KiB, row tile f / 4) fills slots 64 (f % 4) ..
+  // + 63 of its tile, lane p's bytes landing at slot 64 (f % 4) + p: row
+  // r = 4 (f % 4) + p / 16, position p % 16, so lane p fetches chunk
+  // (p % 16) ^ r and one load reads 4 whole 256-byte rows (fragment order,
+  // 16 rows x 64 bytes per load, is served at well under half the rate).
+  // Fragment (row tile i, k step j) = row l16, chunk 4 j + quad: one
+  // conflict-free ds_read_b128.  Rows past M read row M - 1 (never stored).
+  static_assert(STEPS == 4, "16 chunks per row, 4 loads per row tile");
   auto load_x = [&](int st, int buf) {
 #pragma unroll
     for (int j = 0; j < XPW; ++j) {
       const int f = wave * XPW + j;
-      const int rr = min(16 * (f / STEPS) + l16, rows_left);
-      const int k = st * 256 + 64 * (f % STEPS) + 16 * quad;
+      const int r = 4 * (f % 4) + quad;
+      const int rr = min(16 * (f / 4) + r, rows_left);
+      const int k = st * 256 + 16 * (l16 ^ r);
       __builtin_amdgcn_global_load_lds((const void*)(x + (size_t)(m0 + rr) * K + k),
                                        (__attribute__((address_space(3))) void*)(&xa[buf][f * 64]),
                                        16, 0, 0);
@@ -164,7 +172,9 @@ __global__ __launch_bounds__(256) void i8t2_gemm_kernel(const int8_t* __restrict
     // overlaps the MFMAs of the tiles in between
     const u32x4_t* xs = &xa[buf][0];
     constexpr int NF = MT * STEPS;
-    auto frag = [&](int c) { return xs[((c % MT) * STEPS + c / MT) * 64 + lane]; };
+    auto frag = [&](int c) {
+      return xs[256 * (c % MT) + 16 * l16 + ((4 * (c / MT) + quad) ^ l16)];
+    };
     u32x4_t ar[3];
     ar[0] = frag(0);
     if (NF > 1) ar[1] = frag(1);
