@@ -81,7 +81,10 @@ def test_gemm_lowbit_exact_probe_bit_exact(M, N, K, w_bit, gs, xdt, sym):
     assert np.array_equal(y.astype(np.float64), y_ref)
 
 
-@pytest.mark.parametrize("M,N,K,xdt", [(16, 32, 1024, si.BF16), (48, 16, 2048, si.F16)])
+@pytest.mark.parametrize("M,N,K,xdt", [(16, 32, 1024, si.BF16), (48, 16, 2048, si.F16),
+                                        # odd count of 64-deep blocks: the last 128-deep
+                                        # stage is half past K and its k steps are skipped
+                                        (16, 32, 192, si.BF16), (33, 48, 320, si.F16)])
 def test_gemm_int8_exact_probe_bit_exact(M, N, K, xdt):
     case = si.exact_int8_case(M, N, K, xdt, seed=N + 1)
     y = run_gemm(case)
