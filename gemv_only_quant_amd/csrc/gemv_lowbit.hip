@@ -185,24 +185,34 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lowbit_kernel(
     }
   }
 
-  // 7. sum the 16 row-lanes of each column quad in the wave, then the waves
+  // 7. sum the row-lanes of each column quad: with 4 quads, two DPP row
+  // rotations (by 4 and 8 lanes) sum the 4 row-lanes of a quad inside each
+  // 16-lane row, and the rows' and waves' partials meet in LDS (no
+  // cross-row shuffle); otherwise cross-lane shuffles sum the whole wave
+  constexpr int PARTS = CQ == 4 ? 4 : 1;  // partials per wave left for LDS
 #pragma unroll
   for (int m = 0; m < MB; ++m)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       float v = r[m][c];
+      if constexpr (CQ == 4) {
+        v = dpp_add<0x124, 0xF>(v);  // row_ror:4
+        v = dpp_add<0x128, 0xF>(v);  // row_ror:8
+      } else {
 #pragma unroll
-      for (int b = CQ; b < 64; b *= 2) v += __shfl_xor(v, b);
+        for (int b = CQ; b < 64; b *= 2) v += __shfl_xor(v, b);
+      }
       r[m][c] = v;
     }
   __syncthreads();
-  float* red = reinterpret_cast<float*>(xl);  // [WAVES][MB][CW]
-  static_assert(WAVES * MB * CW <= MB * GROUPS * GSTRIDE, "LDS reuse");
-  if (lane < CQ) {
+  float* red = reinterpret_cast<float*>(xl);  // [WAVES * PARTS][MB][CW]
+  static_assert(WAVES * PARTS * MB * CW <= MB * GROUPS * GSTRIDE, "LDS reuse");
+  if ((lane & 15) < CQ && (PARTS == 4 || lane < CQ)) {
+    const int part = wave * PARTS + (PARTS == 4 ? lane >> 4 : 0);
 #pragma unroll
     for (int m = 0; m < MB; ++m)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) red[(wave * MB + m) * CW + cq * 4 + c] = r[m][c];
+      for (int c = 0; c < 4; ++c) red[(part * MB + m) * CW + cq * 4 + c] = r[m][c];
   }
   __syncthreads();
   auto store = [&](auto* yt) {
@@ -213,7 +223,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lowbit_kernel(
       if (m < M && n < N) {
         float sum = 0.f;
 #pragma unroll
-        for (int v = 0; v < WAVES; ++v) sum += red[(v * MB + m) * CW + col];
+        for (int v = 0; v < WAVES * PARTS; ++v) sum += red[(v * MB + m) * CW + col];
         yt[(size_t)m * N + n] = (T)sum;
       }
     }
