@@ -719,19 +719,45 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
     for (int s = 0; s < NT; ++s) asm volatile("" : "+a"(acc[i][s]));
   __builtin_amdgcn_sched_barrier(0);
 
+  // y goes out through LDS, one 16-row tile at a time: the wave's 16 x 64
+  // block is written row-major into its own LDS region (row stride 68
+  // floats: both the column-wise writes and the row-wise reads hit 64
+  // distinct banks), then read back so that each store instruction covers
+  // 4 whole rows of the block (16 lanes x 4 columns per row) with 16-byte
+  // (fp32) or 8-byte (16-bit) stores: every row segment leaves as whole
+  // 128-byte lines (direct stores from
+  // the accumulator layout write 64-byte halves, measured 1.27x the
+  // output's bytes in HBM writes).  The x buffers are free: the K loop
+  // ended with a barrier.  A wave's LDS operations run in order, so the
+  // region needs no barrier between tiles.
+  float* const yl = reinterpret_cast<float*>(&xa[0][0]) + wave * (16 * 68);
+  const int prow = lane >> 4, pcol = 4 * (lane & 15);  // row within 4, first column
+  const bool pcol_ok = s0 + ((lane & 15) >> 2) < strips;
   with_y(y, ydt, [&](auto* yt) {
     using T = typename std::remove_pointer<decltype(yt)>::type;
 #pragma unroll
-    for (int s = 0; s < NT; ++s) {
-      if (s0 + s >= strips) continue;
-      const int n = 16 * (s0 + s) + l16;
+    for (int i = 0; i < MT; ++i) {
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
+      for (int s = 0; s < NT; ++s)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + 16 * i + 4 * quad + r;
-          if (m < M) yt[(size_t)m * N + n] = (T)acc[i][s][r];
+        for (int r = 0; r < 4; ++r) yl[(4 * quad + r) * 68 + 16 * s + l16] = acc[i][s][r];
+      f32x4_t v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[j] = *reinterpret_cast<const f32x4_t*>(yl + (4 * j + prow) * 68 + pcol);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = m0 + 16 * i + 4 * j + prow;
+        if (m < M && pcol_ok) {
+          T* dst = yt + (size_t)m * N + 16 * s0 + pcol;
+          if constexpr (std::is_same<T, float>::value) {
+            *reinterpret_cast<f32x4_t*>(dst) = v[j];
+          } else {
+            T t[4] = {(T)v[j][0], (T)v[j][1], (T)v[j][2], (T)v[j][3]};
+            *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, t);
+          }
         }
+      }
     }
   });
 }
