@@ -225,17 +225,45 @@ __global__ __launch_bounds__(256) void i8t2_gemm_kernel(const int8_t* __restrict
     for (int s = 0; s < NT4; ++s) asm volatile("" : "+a"(acc[i][s]));
   __builtin_amdgcn_sched_barrier(0);
 
+  if constexpr (NT4 == 4) {
+    // y through LDS per 16-row tile, as the low-bit prefill does: the
+    // wave's 16 x 64 block goes in row-major (row stride 68 words, no bank
+    // conflicts either way) and leaves as 4 whole rows per store
+    // instruction (16 lanes x 16 bytes per row), i.e. whole 128-byte lines.
+    // The x buffers are free (the K loop ended with a barrier).
+    int32_t* const yl = reinterpret_cast<int32_t*>(&xa[0][0]) + wave * (16 * 68);
+    const int prow = lane >> 4, pcol = 4 * (lane & 15);
+    const bool pcol_ok = s0 + ((lane & 15) >> 2) < strips;
 #pragma unroll
-  for (int s = 0; s < NT4; ++s) {
-    if (s0 + s >= strips) continue;
-    const int n = 16 * (s0 + s) + l16;
+    for (int i = 0; i < MT; ++i) {
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+      for (int s = 0; s < NT4; ++s)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 16 * i + 4 * quad + r;
-        if (m < M) y[(size_t)m * N + n] = acc[i][s][r];
+        for (int r = 0; r < 4; ++r) yl[(4 * quad + r) * 68 + 16 * s + l16] = acc[i][s][r];
+      i32x4_t v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[j] = *reinterpret_cast<const i32x4_t*>(yl + (4 * j + prow) * 68 + pcol);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int m = m0 + 16 * i + 4 * j + prow;
+        if (m < M && pcol_ok)
+          *reinterpret_cast<i32x4_t*>(y + (size_t)m * N + 16 * s0 + pcol) = v[j];
       }
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < NT4; ++s) {
+      if (s0 + s >= strips) continue;
+      const int n = 16 * (s0 + s) + l16;
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + 16 * i + 4 * quad + r;
+          if (m < M) y[(size_t)m * N + n] = acc[i][s][r];
+        }
+    }
   }
 }
 
