@@ -113,6 +113,8 @@ GEMM_BAD = [
     (dict(y=MIS), E_ARG, "aligned"),
     # skinny kernel: 32-bit byte offsets into the scale table (2^14 groups x 2^16 columns)
     (dict(M=16, N=65536, K=524288, group_size=32), E_UNS, "too large"),
+    # skinny kernel: 32-bit byte offsets into x (64 rows of K)
+    (dict(M=16, N=64, K=1 << 24, group_size=128), E_UNS, "K=16777216 too large"),
 ]
 
 
