@@ -149,9 +149,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
     uint32_t zw[NT];
   };
   // Stage loads are buffer loads through descriptors based at this
-  // workgroup's strips, rows and columns: offsets stay 32-bit for any
-  // problem size, and a strip or row past the edge reads zeros (the
-  // hardware range check) instead of needing a clamped index.  They are
+  // workgroup's strips, rows and columns: offsets stay within 32 bits (the
+  // host refuses K >= 2^24 and scale tables of 2^30 entries or more), and a
+  // strip or row past the edge reads zeros (the hardware range check)
+  // instead of needing a clamped index.  They are
   // intrinsic calls, so the compiler keeps each one where it is written: a
   // plain load that is only used after the loop's back edge gets moved down
   // to its use, which empties the ring.  Raw values go into the ring; every
