@@ -39,6 +39,8 @@ def lib():
         L.orc_dequant.argtypes = [P, P, P, I, I, I, I, P]
         L.orc_qmm.argtypes = [P, I, P, P, P, I, I, I, I, I, P, P]
         L.orc_qmm_at.argtypes = [P, I, P, P, P, I, I, I, I, I, I, P, P, P, P]
+        L.orc_qmm_mt.argtypes = [P, I, P, P, P, I, I, I, I, I, P, P, I]
+        L.orc_i8t2_mm_mt.argtypes = [P, P, I, I, I, P, I]
         L.orc_mfma_locate.argtypes = [I, I, I, I, I, ctypes.POINTER(S), ctypes.POINTER(I)]
         L.orc_mfma_bytes.argtypes = [I, I, I]
         L.orc_mfma_bytes.restype = S
@@ -135,6 +137,28 @@ def qmm(x_bits, x_dtype, Q, scales, zeros, M, N, K, w_bit, group_size):
     return y, ab
 
 
+def host_threads():
+    """Host threads for the threaded calls: the CPUs this process may run on,
+    at most 16 (a GPU machine's CPU share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def qmm_mt(x_bits, x_dtype, Q, scales, zeros, M, N, K, w_bit, group_size, threads=None):
+    """qmm() with the columns divided over host threads: bit-identical results."""
+    x = _c(x_bits, np.uint16)
+    Q, scales, zeros = _operands(Q, scales, zeros, w_bit)
+    y = np.empty((M, N), np.float64)
+    ab = np.empty((M, N), np.float64)
+    _check(lib().orc_qmm_mt(_ptr(x), x_dtype, _ptr(Q), _ptr(scales), _ptr(zeros),
+                            M, N, K, w_bit, group_size, _ptr(y), _ptr(ab),
+                            threads or host_threads()), "qmm_mt")
+    return y, ab
+
+
 def qmm_at(x_bits, x_dtype, Q, scales, zeros, M, N, K, w_bit, group_size, ms, ns):
     """(y_ref, abs_ref) at the outputs (ms[i], ns[i]) only."""
     x = _c(x_bits, np.uint16)
@@ -189,6 +213,17 @@ def i8t2_mm(A, Wp, M, N, K):
     if rc == -2:
         raise ValueError("oracle i8t2_mm: a sum leaves the int32 range")
     _check(rc, "i8t2_mm")
+    return C
+
+
+def i8t2_mm_mt(A, Wp, M, N, K, threads=None):
+    """i8t2_mm() with the columns divided over host threads (exact either way)."""
+    A, Wp = _c(A, np.int8), _c(Wp, np.uint8)
+    C = np.zeros((M, N), np.int32)
+    rc = lib().orc_i8t2_mm_mt(_ptr(A), _ptr(Wp), M, N, K, _ptr(C), threads or host_threads())
+    if rc == -2:
+        raise ValueError("oracle i8t2_mm_mt: a sum leaves the int32 range")
+    _check(rc, "i8t2_mm_mt")
     return C
 
 

@@ -17,7 +17,7 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     # -ffp-contract=off: every product and sum is rounded as written.
     cmd = ["gcc", "-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math",
-           "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
+           "-fPIC", "-shared", "-pthread", "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -27,6 +27,7 @@
 #include "qmm_oracle.h"
 
 #include <math.h>
+#include <pthread.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -173,22 +174,23 @@ static double row_scale(const void* scales, int w_bit, int n) {
     return w_bit == 8 ? (double)((const float*)scales)[n] : 1.0;
 }
 
-int orc_qmm(const uint16_t* x, int x_dtype, const void* Q, const void* scales,
-            const int32_t* zeros, int M, int N, int K, int w_bit, int group_size,
-            double* y_ref, double* abs_ref) {
-    if (M < 0 || (x_dtype != 0 && x_dtype != 1)) return -1;
-    if (check_args(N, K, w_bit, group_size, zeros)) return -1;
-    /* Dequantize once into column-major storage wt[n][k] (storage order only). */
-    float* wt = (float*)malloc(sizeof(float) * ((size_t)N * K + 1));
-    double* xr = (double*)malloc(sizeof(double) * ((size_t)K + 1));
-    if (!wt || !xr) { free(wt); free(xr); return -1; }
-    for (int n = 0; n < N; ++n)
+/* Outputs (m, n) for every row m and the columns n0 <= n < n1.  xd is x
+ * decoded to double, (M, K).  The columns are dequantized once into
+ * column-major storage wt[n][k] (storage order only); each output is then
+ * the fp64 sum over k ascending, with the int8 row scale applied after it. */
+static int qmm_columns(const double* xd, const void* Q, const void* scales,
+                       const int32_t* zeros, int M, int N, int K, int w_bit, int group_size,
+                       int n0, int n1, double* y_ref, double* abs_ref) {
+    float* wt = (float*)malloc(sizeof(float) * ((size_t)(n1 - n0) * K + 1));
+    if (!wt) return -1;
+    for (int n = n0; n < n1; ++n)
         for (int k = 0; k < K; ++k)
-            wt[(size_t)n * K + k] = orc_w_at(Q, scales, zeros, N, K, w_bit, group_size, k, n);
+            wt[(size_t)(n - n0) * K + k] =
+                orc_w_at(Q, scales, zeros, N, K, w_bit, group_size, k, n);
     for (int m = 0; m < M; ++m) {
-        for (int k = 0; k < K; ++k) xr[k] = x_at(x, x_dtype, K, m, k);
-        for (int n = 0; n < N; ++n) {
-            const float* w = wt + (size_t)n * K;
+        const double* xr = xd + (size_t)m * K;
+        for (int n = n0; n < n1; ++n) {
+            const float* w = wt + (size_t)(n - n0) * K;
             double s = row_scale(scales, w_bit, n);
             double acc = 0.0, ab = 0.0;
             for (int k = 0; k < K; ++k) {
@@ -201,8 +203,27 @@ int orc_qmm(const uint16_t* x, int x_dtype, const void* Q, const void* scales,
         }
     }
     free(wt);
-    free(xr);
     return 0;
+}
+
+static double* decode_x(const uint16_t* x, int x_dtype, int M, int K) {
+    double* xd = (double*)malloc(sizeof(double) * ((size_t)M * K + 1));
+    if (!xd) return NULL;
+    for (int m = 0; m < M; ++m)
+        for (int k = 0; k < K; ++k) xd[(size_t)m * K + k] = x_at(x, x_dtype, K, m, k);
+    return xd;
+}
+
+int orc_qmm(const uint16_t* x, int x_dtype, const void* Q, const void* scales,
+            const int32_t* zeros, int M, int N, int K, int w_bit, int group_size,
+            double* y_ref, double* abs_ref) {
+    if (M < 0 || (x_dtype != 0 && x_dtype != 1)) return -1;
+    if (check_args(N, K, w_bit, group_size, zeros)) return -1;
+    double* xd = decode_x(x, x_dtype, M, K);
+    if (!xd) return -1;
+    int rc = qmm_columns(xd, Q, scales, zeros, M, N, K, w_bit, group_size, 0, N, y_ref, abs_ref);
+    free(xd);
+    return rc;
 }
 
 int orc_qmm_at(const uint16_t* x, int x_dtype, const void* Q, const void* scales,
@@ -320,18 +341,29 @@ int orc_t2_at(const uint8_t* Wp, int N, int K, int k, int n) {
  * integer products, exact (int64 accumulation, k ascending).  Returns -1 on
  * bad sizes, -2 if a sum leaves the int32 range (the page accumulates in
  * int32; no valid input with K < 2^23 gets there). */
-int orc_i8t2_mm(const int8_t* A, const uint8_t* Wp, int M, int N, int K, int32_t* C) {
-    if (M < 0 || N < 0 || K < 0 || K % 4 != 0) return -1;
+static int i8t2_columns(const int8_t* A, const uint8_t* Wp, int M, int N, int K, int n0,
+                        int n1, int32_t* C) {
+    /* each column's values decoded once (storage order only) */
+    int8_t* wc = (int8_t*)malloc((size_t)(n1 - n0) * K + 1);
+    if (!wc) return -1;
+    for (int n = n0; n < n1; ++n)
+        for (int k = 0; k < K; ++k) wc[(size_t)(n - n0) * K + k] = (int8_t)orc_t2_at(Wp, N, K, k, n);
     int rc = 0;
     for (int m = 0; m < M; ++m)
-        for (int n = 0; n < N; ++n) {
+        for (int n = n0; n < n1; ++n) {
+            const int8_t* w = wc + (size_t)(n - n0) * K;
             int64_t acc = 0;
-            for (int k = 0; k < K; ++k)
-                acc += (int64_t)A[(size_t)m * K + k] * orc_t2_at(Wp, N, K, k, n);
+            for (int k = 0; k < K; ++k) acc += (int64_t)A[(size_t)m * K + k] * w[k];
             if (acc > INT32_MAX || acc < INT32_MIN) rc = -2;
             C[(size_t)m * N + n] = (int32_t)acc;
         }
+    free(wc);
     return rc;
+}
+
+int orc_i8t2_mm(const int8_t* A, const uint8_t* Wp, int M, int N, int K, int32_t* C) {
+    if (M < 0 || N < 0 || K < 0 || K % 4 != 0) return -1;
+    return i8t2_columns(A, Wp, M, N, K, 0, N, C);
 }
 
 /* The same for `count` chosen outputs (ms[i], ns[i]). */
@@ -346,6 +378,113 @@ int orc_i8t2_mm_at(const int8_t* A, const uint8_t* Wp, int M, int N, int K, int 
         C[i] = (int32_t)acc;
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Threaded driver: the products above over column slices on several   */
+/* host threads.  Each output is computed by the same column function   */
+/* with the same arithmetic as the single-threaded call, so the results */
+/* are bit-identical; only the work is divided (64-column chunks dealt  */
+/* round-robin to the threads).                                          */
+/* ------------------------------------------------------------------ */
+enum { ORC_CHUNK = 64 };
+
+struct orc_job {
+    int ternary;
+    const double* xd;                 /* low-bit / int8: x decoded to double */
+    const int8_t* A;                  /* ternary: int8 activations */
+    const void* Q;
+    const void* scales;
+    const int32_t* zeros;
+    int M, N, K, w_bit, group_size;
+    double* y_ref;
+    double* abs_ref;
+    int32_t* C;
+    int tid, threads, rc;
+};
+
+static void* orc_worker(void* arg) {
+    struct orc_job* j = (struct orc_job*)arg;
+    int chunks = (j->N + ORC_CHUNK - 1) / ORC_CHUNK;
+    for (int c = j->tid; c < chunks; c += j->threads) {
+        int n0 = c * ORC_CHUNK, n1 = n0 + ORC_CHUNK < j->N ? n0 + ORC_CHUNK : j->N;
+        int rc = j->ternary
+                     ? i8t2_columns(j->A, (const uint8_t*)j->Q, j->M, j->N, j->K, n0, n1, j->C)
+                     : qmm_columns(j->xd, j->Q, j->scales, j->zeros, j->M, j->N, j->K, j->w_bit,
+                                   j->group_size, n0, n1, j->y_ref, j->abs_ref);
+        if (rc == -1 || (rc != 0 && j->rc == 0)) j->rc = rc;
+    }
+    return NULL;
+}
+
+/* Runs `threads` workers on copies of *proto; the first failure wins
+ * (-1 allocation, -2 int32 range). */
+static int orc_run(const struct orc_job* proto, int threads) {
+    if (threads < 1) threads = 1;
+    if (threads > 256) threads = 256;
+    struct orc_job jobs[256];
+    pthread_t tids[256];
+    int started = 0, rc = 0;
+    for (int t = 0; t < threads; ++t) {
+        jobs[t] = *proto;
+        jobs[t].tid = t;
+        jobs[t].threads = threads;
+        jobs[t].rc = 0;
+    }
+    for (int t = 1; t < threads; ++t) {
+        if (pthread_create(&tids[t], NULL, orc_worker, &jobs[t]) != 0) break;
+        started = t;
+    }
+    /* chunks of workers that could not be started are done here */
+    for (int t = started + 1; t < threads; ++t) {
+        jobs[t].threads = threads;
+        orc_worker(&jobs[t]);
+    }
+    orc_worker(&jobs[0]);
+    for (int t = 1; t <= started; ++t) pthread_join(tids[t], NULL);
+    for (int t = 0; t < threads; ++t)
+        if (jobs[t].rc == -1 || (jobs[t].rc != 0 && rc == 0)) rc = jobs[t].rc;
+    return rc;
+}
+
+int orc_qmm_mt(const uint16_t* x, int x_dtype, const void* Q, const void* scales,
+               const int32_t* zeros, int M, int N, int K, int w_bit, int group_size,
+               double* y_ref, double* abs_ref, int threads) {
+    if (M < 0 || (x_dtype != 0 && x_dtype != 1)) return -1;
+    if (check_args(N, K, w_bit, group_size, zeros)) return -1;
+    double* xd = decode_x(x, x_dtype, M, K);
+    if (!xd) return -1;
+    struct orc_job j;
+    memset(&j, 0, sizeof j);
+    j.xd = xd;
+    j.Q = Q;
+    j.scales = scales;
+    j.zeros = zeros;
+    j.M = M;
+    j.N = N;
+    j.K = K;
+    j.w_bit = w_bit;
+    j.group_size = group_size;
+    j.y_ref = y_ref;
+    j.abs_ref = abs_ref;
+    int rc = orc_run(&j, threads);
+    free(xd);
+    return rc;
+}
+
+int orc_i8t2_mm_mt(const int8_t* A, const uint8_t* Wp, int M, int N, int K, int32_t* C,
+                   int threads) {
+    if (M < 0 || N < 0 || K < 0 || K % 4 != 0) return -1;
+    struct orc_job j;
+    memset(&j, 0, sizeof j);
+    j.ternary = 1;
+    j.A = A;
+    j.Q = Wp;
+    j.M = M;
+    j.N = N;
+    j.K = K;
+    j.C = C;
+    return orc_run(&j, threads);
 }
 
 /* Reference permutation of the ternary weight into this library's tile

@@ -8,8 +8,9 @@
  * benchmark's CPU-baseline leg do.  It shares no code, header, table or
  * constant with the HIP library.
  *
- * Plain, slow, single-threaded C99.  Every decode is written from its
- * definition; the matmul accumulates in fp64 with k ascending.
+ * Plain, slow C99.  Every decode is written from its definition; the matmul
+ * accumulates in fp64 with k ascending.  Single-threaded, except that the
+ * *_mt calls hand the same per-output work to several host threads.
  *
  * Operand conventions (all arrays contiguous, row-major):
  *   x       (M, K) 16-bit words, fp16 (x_dtype 0) or bf16 (x_dtype 1)
@@ -64,6 +65,13 @@ int orc_qmm_at(const uint16_t* x, int x_dtype, const void* Q, const void* scales
                const int32_t* zeros, int M, int N, int K, int w_bit, int group_size,
                int count, const int* ms, const int* ns, double* y_ref, double* abs_ref);
 
+/* The same two products over column slices on `threads` host threads:
+ * identical per-output arithmetic, so bit-identical results.  orc_i8t2_mm_mt
+ * returns -2 if a sum leaves the int32 range. */
+int orc_qmm_mt(const uint16_t* x, int x_dtype, const void* Q, const void* scales,
+               const int32_t* zeros, int M, int N, int K, int w_bit, int group_size,
+               double* y_ref, double* abs_ref, int threads);
+
 /* Reference permutation into the MFMA tile layout, written element by
  * element from the layout specification (see orc_mfma_locate). */
 int orc_mfma_locate(int N, int K, int w_bit, int k, int n, size_t* byte_or_word, int* shift);
@@ -77,6 +85,8 @@ int orc_t2_at(const uint8_t* Wp, int N, int K, int k, int n);
 int orc_i8t2_mm(const int8_t* A, const uint8_t* Wp, int M, int N, int K, int32_t* C);
 int orc_i8t2_mm_at(const int8_t* A, const uint8_t* Wp, int M, int N, int K, int count,
                    const int* ms, const int* ns, int32_t* C);
+int orc_i8t2_mm_mt(const int8_t* A, const uint8_t* Wp, int M, int N, int K, int32_t* C,
+                   int threads);
 /* Reference permutation into the ternary tile layout (see the .c file). */
 size_t orc_t2_tile_bytes(int N, int K);
 int orc_t2_tile_locate(int N, int K, int k, int n, size_t* byte, int* shift);

@@ -1,6 +1,13 @@
-"""Helpers for the GPU parity tests (tolerance check, device transfer)."""
+"""Helpers for the GPU parity tests (tolerance check, device transfer, the
+oracle's full result for the full-size workloads, a parity log)."""
+import json
+import os
+
 import numpy as np
 import torch
+
+import oracle
+import synth_inputs as si
 
 # |y - y_ref| <= 2e-3 * sum_k |x w| + 1e-5, elementwise (the stated bound)
 REL, ABS = 2e-3, 1e-5
@@ -40,3 +47,37 @@ def sample_points(M, N, count, seed):
             ms.append(m)
             ns.append(n)
     return np.array(ms, np.int32), np.array(ns, np.int32)
+
+
+_FULL = {}
+
+
+def full_reference(name):
+    """The oracle's (y_ref, abs_ref) over EVERY output of a full-size workload
+    (threaded over columns, bit-identical to the single-threaded oracle).
+    Results are kept for the session (under 2 GB for every workload), so tests
+    of one workload share one oracle run."""
+    if name not in _FULL:
+        case = si.workload(name)
+        _FULL[name] = oracle.qmm_mt(*case.oracle_args())
+    return _FULL[name]
+
+
+def full_reference_i8t2(name):
+    """The oracle's exact int32 product over every output of a ternary workload."""
+    key = ("i8t2", name)
+    if key not in _FULL:
+        case = si.workload(name)
+        _FULL[key] = oracle.i8t2_mm_mt(case.A.numpy(), case.Wp.numpy(), case.M, case.N, case.K)
+    return _FULL[key]
+
+
+def log_parity(what, **fields):
+    """Print a parity figure and, if QMM_PARITY_LOG names a file, append it
+    there as one JSON line."""
+    rec = dict(case=what, **fields)
+    print(json.dumps(rec), flush=True)
+    path = os.environ.get("QMM_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(rec) + "\n")

@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import synth_inputs as si
-from gpu_util import assert_within_bound, cpu, sample_points
+from gpu_util import assert_within_bound, cpu, full_reference, log_parity
 
 qmm = pytest.importorskip("gemv_only_quant_amd")
 pytestmark = pytest.mark.gpu
@@ -120,22 +120,16 @@ def test_zero_m_leaves_output_untouched():
 # ------------------------------------------------------------ full sizes
 @pytest.mark.parametrize("name", ["int8_gemv_m1_k1024_n1024",
                                   "int4_g128_asym_gemv_m1_k4096_n4096",
-                                  "int4_pc_sym_gemv_m1_k4096_n4096"])
+                                  "int4_pc_sym_gemv_m1_k4096_n4096",
+                                  # the M = 16 workloads through the GEMV path, a
+                                  # cross-check of the matrix-core path
+                                  "int8_skinny_m16_k4096_n14336",
+                                  "int4_g128_sym_m16_k8192_n8192"])
 def test_gemv_full_size_all_outputs(name):
+    """Every output of the full-size workload, in the launch configuration the
+    benchmark times, against the oracle's."""
     case = si.workload(name)
     y = run_gemv(case)
-    y_ref, a_ref = oracle.qmm(*case.oracle_args())
+    y_ref, a_ref = full_reference(name)
     ratio = assert_within_bound(y, y_ref, a_ref, name)
-    print(f"{name}: max err/bound {ratio:.3g}")
-
-
-@pytest.mark.parametrize("name", ["int8_skinny_m16_k4096_n14336", "int4_g128_sym_m16_k8192_n8192"])
-def test_gemv_full_size_sampled(name):
-    """The M = 16 workloads through the GEMV path (cross-check of the MFMA
-    path): sampled outputs against the oracle computed one by one."""
-    case = si.workload(name)
-    y = run_gemv(case)
-    ms, ns = sample_points(case.M, case.N, 256, seed=5)
-    y_ref, a_ref = oracle.qmm_at(*case.oracle_args(), ms, ns)
-    ratio = assert_within_bound(y[ms, ns], y_ref, a_ref, name)
-    print(f"{name}: max err/bound {ratio:.3g}")
+    log_parity(name, entry="qmm_gemv", outputs=int(y.size), max_err_over_bound=ratio)

@@ -1,14 +1,14 @@
 """GPU parity of the int8 x ternary product (liger-kernel mm_int8int2): the
 repack is bit-exact against the oracle's layout reference and inverts
-exactly; the product is integer arithmetic, so every output must equal the
-oracle's exactly."""
+exactly; the product is integer arithmetic, so every output (all of them, at
+full size too) must equal the oracle's exactly."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 import synth_inputs as si
-from gpu_util import cpu, sample_points
+from gpu_util import cpu
 
 qmm = pytest.importorskip("gemv_only_quant_amd")
 pytestmark = pytest.mark.gpu
@@ -68,9 +68,13 @@ def test_i8t2_full_size_decode_all_outputs():
                                             case.K))
 
 
-def test_i8t2_full_size_prefill_sampled():
-    case = si.workload("i8t2_m4096_k4096_n11008")
+def test_i8t2_full_size_prefill_all_outputs():
+    """Every output of the full-size int8 x ternary prefill, exactly."""
+    from gpu_util import full_reference_i8t2, log_parity
+    name = "i8t2_m4096_k4096_n11008"
+    case = si.workload(name)
     y = run(case)
-    ms, ns = sample_points(case.M, case.N, 512, seed=13)
-    want = oracle.i8t2_mm_at(case.A.numpy(), case.Wp.numpy(), case.M, case.N, case.K, ms, ns)
-    assert np.array_equal(y[ms, ns], want)
+    want = full_reference_i8t2(name)
+    mism = int(np.count_nonzero(y != want))
+    log_parity(name, entry="qmm_i8t2_gemm", outputs=int(y.size), mismatches=mism)
+    assert mism == 0

@@ -137,12 +137,16 @@ def test_f32_through_ex_equals_plain_entry():
     assert torch.equal(y1, y2)
 
 
-def test_bf16_output_prefill_sampled():
+def test_bf16_output_prefill_all_outputs():
     """The prefill workload through qmm_gemm_ex with bf16 y, in the launch
-    configuration the benchmark times: sampled outputs against the oracle."""
-    from gpu_util import sample_points
-    case = si.workload("int4_g128_asym_prefill_m4096_k4096_n11008")
+    configuration the benchmark times: every output against the oracle."""
+    from gpu_util import full_reference, log_parity
+    name = "int4_g128_asym_prefill_m4096_k4096_n11008"
+    case = si.workload(name)
     y = run(case, "gemm", "bf16")
-    ms, ns = sample_points(case.M, case.N, 256, seed=11)
-    y_ref, a_ref = oracle.qmm_at(*case.oracle_args(), ms, ns)
-    assert_out_within_bound(y[ms, ns], y_ref, a_ref, "bf16", "prefill bf16 out")
+    y_ref, a_ref = full_reference(name)
+    assert_out_within_bound(y, y_ref, a_ref, "bf16", "prefill bf16 out")
+    u = UNIT["bf16"]
+    bound = (REL * a_ref + ABS) * (1 + u) + u * np.abs(y_ref) + 2.0 ** -24
+    log_parity(name + "_bf16_y", entry="qmm_gemm_ex", outputs=int(y.size),
+               max_err_over_bound=float(np.max(np.abs(y.astype(np.float64) - y_ref) / bound)))

@@ -127,7 +127,7 @@ def test_tile_layout_is_a_bijection(N, K):
 MUTATIONS = [
     ("(k % R) * N + n] >> (2 * (k / R))", "(k / R) * N + n] >> (2 * (k % R))"),  # quarter/row swapped
     ("return code - 1;", "return code;"),                                          # dropped -1
-    ("A[(size_t)m * K + k] * orc_t2_at", "A[(size_t)k * M + m] * orc_t2_at"),      # transposed A
+    ("A[(size_t)m * K + k] * w[k]", "A[(size_t)k * M + m] * w[k]"),              # transposed A
     ("int R = K / 4;", "int R = K / 8 + (K < 8);"),                                # wrong row count
 ]
 
