@@ -2,6 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
     python bench.py --probe WORKLOAD      (three calls, for rocprofv3 --pmc)
+    python bench.py --trace-summary DB    (per-workload rows of a rocprofv3 trace
+                                           taken with --kernel-trace --marker-trace)
 
 A step is one call of the hot path on one batch of synthetic input already
 resident in HBM.  The headline workload is the int4 group-128 asymmetric
@@ -11,14 +13,17 @@ Every other workload is timed the same way and reported under "workloads";
 the prefill GEMM (M=4096) is reported in TFLOP/s under "prefill".
 
 Memory-bound calls rotate over a pool of weight copies (> 2 x the 256 MB
-Infinity Cache), so every call streams its weights from HBM.  The timed
-calls are captured once in a HIP graph and replayed five times, each replay
-bracketed by HIP events on the launch stream; the median replay gives the
-time per call.  "calibration" holds what this GPU reaches on plain work of
+Infinity Cache), and before every timed replay an untimed pass over a 1 GiB
+buffer evicts the cache, so every call streams its weights from HBM whatever
+the number of steps.  The timed calls are captured once in a HIP graph and
+replayed five times, each replay bracketed by HIP events on the launch
+stream; the median replay gives the time per call.  "calibration" holds what this GPU reaches on plain work of
 the same kind (a device-to-device copy, the vendor BLAS's dense bf16 GEMM
 of the prefill shape), labelled as such; the roofline peaks stay the
-published ones.  The CPU baseline times the plain single-threaded oracle on
-the host ("cpu_baseline.sample").  Prints one JSON line.
+published ones.  The CPU baseline times the oracle on the host's cores, on
+the headline product and on bounded row x column samples of every other
+workload, with one thread and with all of them ("cpu_baseline").  Prints
+one JSON line.
 """
 import argparse
 import hashlib
@@ -28,6 +33,8 @@ import re
 import statistics
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -65,6 +72,72 @@ def bytes_of(case, y_bytes=4):
         w += case.zeros.numel() * case.zeros.element_size()
     io = case.x.numel() * case.x.element_size() + case.M * case.N * y_bytes
     return w, w + io
+
+
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class _Marks:
+    """roctx ranges around the timed replays (no-ops unless a tracer such as
+    rocprofv3 --marker-trace is attached), so a kernel trace can be split by
+    workload and restricted to the timed, graph-replayed dispatches."""
+    lib = False
+
+    @classmethod
+    def _get(cls):
+        if cls.lib is False:
+            import ctypes
+            path = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib",
+                                "librocprofiler-sdk-roctx.so")
+            try:
+                cls.lib = ctypes.CDLL(path)
+                cls.lib.roctxRangePushA.argtypes = [ctypes.c_char_p]
+            except OSError:
+                cls.lib = None
+        return cls.lib
+
+    @classmethod
+    def push(cls, label):
+        if cls._get() is not None:
+            cls.lib.roctxRangePushA(label.encode())
+
+    @classmethod
+    def pop(cls):
+        if cls._get() is not None:
+            cls.lib.roctxRangePop()
+
+
+_EVICT = []
+
+
+def evict_cache():
+    """Untimed: read and write a 1 GiB buffer (4x the 256 MB Infinity Cache),
+    so no weight copy of the next timed replay is still cached."""
+    import torch
+    if not _EVICT:
+        _EVICT.append(torch.zeros(1 << 30, dtype=torch.uint8, device="cuda"))
+    _EVICT[0].add_(1)
+
+
+def replay_us(graph, steps, label, reps=5):
+    """Median µs per call over `reps` timed replays of a `steps`-call graph,
+    each after a cache eviction, bracketed by events on the launch stream and
+    by a roctx range named `timed <label>`."""
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    out = []
+    for _ in range(reps):
+        evict_cache()
+        torch.cuda.synchronize()
+        _Marks.push(f"timed {label}")
+        start.record()
+        graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        _Marks.pop()
+        out.append(start.elapsed_time(end) * 1e3 / steps)
+    return statistics.median(out)
 
 
 def time_workload(name, steps, warmup, path, out="f32"):
@@ -122,18 +195,12 @@ def time_workload(name, steps, warmup, path, out="f32"):
     torch.cuda.synchronize()
     assert torch.equal(y_graph, y), f"{name}: graph replay differs from eager call"
 
-    reps = []
-    for _ in range(5):
-        torch.cuda.synchronize()
-        start.record()
-        graph.replay()
-        end.record()
-        torch.cuda.synchronize()
-        reps.append(start.elapsed_time(end) * 1e3 / steps)
-    us = statistics.median(reps)
+    us = replay_us(graph, steps, f"{name} {out}")
     del graph, pool
+    progress(f"{name} ({out} y): {us:.3f} us per call")
     return dict(case=case, us=us, eager_us=eager_us, wbytes=wbytes, tbytes=tbytes,
-                flops=2.0 * case.M * case.N * case.K, copies=copies)
+                flops=2.0 * case.M * case.N * case.K, copies=copies,
+                rotated=min(steps, copies), rotated_bytes=min(steps, copies) * wbytes)
 
 
 def calibration():
@@ -205,17 +272,9 @@ def time_ternary(name, steps, warmup):
             call(i)
     graph.replay()
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = []
-    for _ in range(5):
-        torch.cuda.synchronize()
-        start.record()
-        graph.replay()
-        end.record()
-        torch.cuda.synchronize()
-        reps.append(start.elapsed_time(end) * 1e3 / steps)
-    us = statistics.median(reps)
+    us = replay_us(graph, steps, name)
     del graph, pool
+    progress(f"{name}: {us:.3f} us per call")
     tops = 2.0 * case.M * case.N * case.K / us / 1e6
     return {"workload": name, "entry": "qmm_i8t2_gemm", "us_per_call": round(us, 3),
             "tops": round(tops, 2), "peak_tops": INT8_PEAK_TOPS,
@@ -248,16 +307,8 @@ def time_quantize(K, N, w_bit, group_size, steps=20):
             call()
     graph.replay()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = []
-    for _ in range(5):
-        torch.cuda.synchronize()
-        a.record()
-        graph.replay()
-        b.record()
-        torch.cuda.synchronize()
-        reps.append(a.elapsed_time(b) * 1e3 / steps)
-    us = statistics.median(reps)
+    us = replay_us(graph, steps, f"rtn_int{w_bit}_g{group_size}_fp16_k{K}_n{N}")
+    progress(f"quantize K={K} N={N}: {us:.3f} us per call")
     nbytes = W.numel() * 2 + qw.numel() * 4 + sc.numel() * 2 + qz.numel() * 4
     return {"workload": f"rtn_int{w_bit}_g{group_size}_fp16_k{K}_n{N}", "entry": "qmm_quantize",
             "us_per_call": round(us, 2), "GBps": round(nbytes / us / 1e3, 1),
@@ -284,28 +335,90 @@ def traffic_for(name):
     return None
 
 
-def cpu_baseline(name, budget_s=10.0):
-    import oracle
-    import synth_inputs as si
-    case = si.workload(name)
-    args = case.oracle_args()
-    wbytes, _ = bytes_of(case)
+def host_info():
+    model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
+
+
+def _timed(fn, budget_s):
+    """(seconds per run, runs): fn repeated until budget_s has passed."""
     t0 = time.perf_counter()
-    reps = 0
+    runs = 0
     while True:
-        oracle.qmm(*args)
-        reps += 1
+        fn()
+        runs += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
-            break
-    t = el / reps
-    return {"value": round(wbytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full {name} products (fp64 oracle, 1 thread), {t:.3f} s each"}
+            return el / runs, runs
+
+
+def _sample_args(case, m_s, n_s):
+    """Oracle arguments of rows [0, m_s) and columns [0, n_s) of a workload."""
+    x, xdt, Q, S, Z, M, N, K, wb, gs = case.oracle_args()
+    x = x[:m_s]
+    if wb == 8:
+        Q, S = Q[:n_s], S[:n_s]
+    else:
+        Q, S = Q[:, :n_s], S[:, :n_s]
+        Z = None if Z is None else Z[:, :n_s]
+    return (x, xdt, Q, S, Z, m_s, n_s, K, wb, gs)
+
+
+def cpu_baseline(budget_s=4.0):
+    """The oracle on the host's cores.  value: the headline product (every
+    output, full size) on all threads; then, per workload, a bounded sample
+    (at most 256 rows x 1024 columns, full K) on one thread and on all of them,
+    scaled to the whole workload's outputs."""
+    import oracle
+    import synth_inputs as si
+    threads = oracle.host_threads()
+    progress(f"cpu baseline on {threads} threads")
+    case = si.workload(HEADLINE)
+    args = case.oracle_args()
+    wbytes, _ = bytes_of(case)
+    t_all, runs_all = _timed(lambda: oracle.qmm_mt(*args, threads=threads), budget_s)
+    t_one, runs_one = _timed(lambda: oracle.qmm(*args), budget_s)
+    per = []
+    for name, _ in OTHERS + [(n, None) for n, _ in PREFILL[:2]]:
+        c = si.workload(name)
+        m_s, n_s = min(c.M, 256), min(c.N, 1024)
+        sargs = _sample_args(c, m_s, n_s)
+        s1, _ = _timed(lambda: oracle.qmm(*sargs), 0.5)
+        sa, _ = _timed(lambda: oracle.qmm_mt(*sargs, threads=threads), 0.5)
+        scale = (c.M * c.N) / (m_s * n_s)
+        per.append({"workload": name, "sample": f"{m_s} rows x {n_s} columns, K={c.K}",
+                    "s_per_call_1_thread": round(s1 * scale, 4),
+                    "s_per_call_all_threads": round(sa * scale, 4)})
+    t2 = si.workload(TERNARY[1])
+    m_s, n_s = 256, 1024
+    A = t2.A.numpy()[:m_s]
+    Wp = np.ascontiguousarray(t2.Wp.numpy()[:, :n_s])
+    s1, _ = _timed(lambda: oracle.i8t2_mm(A, Wp, m_s, n_s, t2.K), 0.5)
+    sa, _ = _timed(lambda: oracle.i8t2_mm_mt(A, Wp, m_s, n_s, t2.K, threads=threads), 0.5)
+    scale = (t2.M * t2.N) / (m_s * n_s)
+    per.append({"workload": TERNARY[1], "sample": f"{m_s} rows x {n_s} columns, K={t2.K}",
+                "s_per_call_1_thread": round(s1 * scale, 4),
+                "s_per_call_all_threads": round(sa * scale, 4)})
+    return {"value": round(wbytes / t_all / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{runs_all} full {HEADLINE} products on {threads} threads "
+                      f"({t_all:.4f} s each; fp64 oracle, columns divided over threads)",
+            "single_thread": {"value": round(wbytes / t_one / 1e9, 4), "unit": "GB/s",
+                              "s_per_call": round(t_one, 4), "runs": runs_one},
+            "host": host_info(), "per_workload": per}
 
 
 def line(r, path):
     case, us = r["case"], r["us"]
     out = {"workload": case.name, "entry": f"qmm_{path}", "us_per_call": round(us, 3),
+           "weight_copies_rotated": r["rotated"], "rotated_MB": round(r["rotated_bytes"] / 1e6, 1),
            "weight_GBps": round(r["wbytes"] / us / 1e3, 1),
            "hbm_frac": round(r["tbytes"] / us / 1e3 / HBM_PEAK_GBS, 4),
            "tflops": round(r["flops"] / us / 1e6, 2),
@@ -349,6 +462,36 @@ def probe(name):
     print(f"probe {name}: 3 x qmm_{path} ({copies} weight copies), 3 x 256 MiB copy", flush=True)
 
 
+def trace_summary(db_path):
+    """Per-workload kernel durations from a rocprofv3 trace of this script run
+    with --kernel-trace --marker-trace: only the dispatches inside a `timed
+    <workload>` range (the graph replays that give each time per call) count.
+    Prints a Markdown table: dispatches, mean, median, p90, min, max (µs)."""
+    import sqlite3
+    c = sqlite3.connect(db_path)
+    regions = c.execute("select name, start, end from regions where name like 'timed %' "
+                        "order by start").fetchall()
+    kern = c.execute("select name, start, end from kernels order by start").fetchall()
+    by = {}
+    j = 0
+    for label, r0, r1 in regions:
+        while j < len(kern) and kern[j][1] < r0:
+            j += 1
+        k = j
+        while k < len(kern) and kern[k][1] <= r1:
+            name = re.sub(r"\(.*", "", kern[k][0])
+            by.setdefault((label[6:], name), []).append((kern[k][2] - kern[k][1]) / 1e3)
+            k += 1
+    print("| workload (timed replays) | kernel | dispatches | mean µs | median µs | p90 µs | "
+          "min µs | max µs |")
+    print("|---|---|---|---|---|---|---|---|")
+    for (label, name), d in by.items():
+        d = sorted(d)
+        p90 = d[min(len(d) - 1, int(0.9 * len(d)))]
+        print(f"| {label} | `{name}` | {len(d)} | {statistics.mean(d):.3f} | "
+              f"{statistics.median(d):.3f} | {p90:.3f} | {d[0]:.3f} | {d[-1]:.3f} |")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -358,7 +501,12 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline only")
     ap.add_argument("--probe", metavar="WORKLOAD",
                     help="three calls of one workload and a 256 MiB copy, for counter runs")
+    ap.add_argument("--trace-summary", metavar="DB",
+                    help="per-workload kernel durations from a rocprofv3 trace database")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the kernels run on a single device; the design notes describe sharding)",
@@ -390,7 +538,9 @@ def main():
         "config": {"workload": HEADLINE, "M": case.M, "N": case.N, "K": case.K,
                    "w_bit": case.w_bit, "group_size": case.group_size,
                    "zeros": case.zeros is not None, "accumulate": "f32", "entry": "qmm_gemv",
-                   "weight_pool_copies": r["copies"], "timing": "hip graph replay",
+                   "weight_pool_copies": r["copies"], "weight_copies_rotated": r["rotated"],
+                   "rotated_MB": round(r["rotated_bytes"] / 1e6, 1),
+                   "timing": "hip graph replay, 1 GiB cache eviction before each timed replay",
                    "eager_us_per_call": round(r["eager_us"], 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -417,7 +567,7 @@ def main():
         out["quantize"] = [time_quantize(4096, 4096, 4, 128)]
         out["calibration"] = calibration()
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(HEADLINE)
+        out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
 
 

@@ -61,20 +61,87 @@ class QmmError(ValueError):
         self.status = status
 
 
-def _ptr(t):
-    if t is None:
-        return None
-    if isinstance(t, int):
-        return t
-    return t.data_ptr()
-
-
-def _stream(stream):
+def _stream(stream, device=None):
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        return torch.cuda.current_stream(device).cuda_stream
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+class _Args:
+    """Pointer extraction with the checks the kernels rely on: each tensor is
+    of an allowed dtype, contiguous and holds at least the bytes the sizes call
+    for (checked as it is taken), and all of them sit on one GPU (checked by
+    stream(), the last step before the call).  So a bad tensor raises QmmError
+    and the library is never called.  None and raw integer pointers pass
+    through unchecked."""
+
+    def __init__(self, fn):
+        self.fn = fn
+        self.tensors = []
+
+    def __call__(self, t, name, nbytes=0, dtypes=None):
+        if t is None or isinstance(t, int):
+            return t
+        if not isinstance(t, torch.Tensor):
+            raise QmmError(QMM_ERR_ARG, f"{self.fn}: {name} must be a tensor, an int or None")
+        if dtypes is not None and t.dtype not in dtypes:
+            want = " or ".join(str(d).replace("torch.", "") for d in dtypes)
+            raise QmmError(QMM_ERR_ARG, f"{self.fn}: {name} must be {want}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise QmmError(QMM_ERR_ARG, f"{self.fn}: {name} must be contiguous")
+        have = t.numel() * t.element_size()
+        if have < nbytes:
+            raise QmmError(QMM_ERR_ARG, f"{self.fn}: {name} holds {have} bytes, "
+                                        f"{nbytes} needed")
+        self.tensors.append((name, t))
+        return t.data_ptr()
+
+    def stream(self, stream):
+        """The device checks, then the stream to launch on (by default the
+        current stream of the operands' device)."""
+        device = None
+        for name, t in self.tensors:
+            if not t.is_cuda:
+                raise QmmError(QMM_ERR_ARG, f"{self.fn}: {name} must be a GPU tensor "
+                                            f"(got {t.device})")
+            if device is None:
+                device = t.device
+            elif t.device != device:
+                raise QmmError(QMM_ERR_ARG, f"{self.fn}: {name} is on {t.device}, other "
+                                            f"operands on {device}")
+        return _stream(stream, device)
+
+
+_F16S = (torch.float16, torch.bfloat16)
+_I8S = (torch.int8, torch.uint8)
+_YS = (torch.float32, torch.float16, torch.bfloat16)
+
+
+def _operand_bytes(M, N, K, w_bit, group_size):
+    """Bytes of x, Q, scales and zeros for the sizes (0 where the sizes are
+    themselves invalid: the library reports those)."""
+    if min(M, N, K) <= 0 or w_bit not in (2, 4, 8):
+        return 0, 0, 0, 0
+    if w_bit == 8:
+        return M * K * 2, N * K, N * 4, 0
+    pack = 32 // w_bit
+    if group_size == QMM_PER_COLUMN:
+        G = 1
+    elif group_size > 0 and K % group_size == 0:
+        G = K // group_size
+    else:
+        G = 0
+    return M * K * 2, N * K * w_bit // 8, G * N * 2, -(-G // pack) * N * 4
+
+
+def _weight_dtypes(w_bit):
+    return _I8S if w_bit == 8 else (torch.int32,)
+
+
+def _scale_dtypes(w_bit):
+    return (torch.float32,) if w_bit == 8 else (torch.float16,)
 
 
 def _check(status):
@@ -109,34 +176,56 @@ def qmm_workspace_bytes(M, N, K, w_bit, group_size):
     return _lib.qmm_workspace_bytes(M, N, K, w_bit, group_size)
 
 
+def _layout_call(fn, name, src, dst, N, K, w_bit, stream):
+    a = _Args(name)
+    nb = max(N, 0) * max(K, 0) * w_bit // 8 if w_bit in (2, 4, 8) else 0
+    ps = a(src, "source", nb, _weight_dtypes(w_bit))
+    pd = a(dst, "destination", nb, _weight_dtypes(w_bit))
+    _check(fn(ps, pd, N, K, w_bit, a.stream(stream)))
+
+
 def qmm_pack(Q_canon, Q_mfma, N, K, w_bit, stream=None):
-    _check(_lib.qmm_pack(_ptr(Q_canon), _ptr(Q_mfma), N, K, w_bit, _stream(stream)))
+    _layout_call(_lib.qmm_pack, "qmm_pack", Q_canon, Q_mfma, N, K, w_bit, stream)
 
 
 def qmm_unpack_layout(Q_mfma, Q_canon, N, K, w_bit, stream=None):
-    _check(_lib.qmm_unpack_layout(_ptr(Q_mfma), _ptr(Q_canon), N, K, w_bit, _stream(stream)))
+    _layout_call(_lib.qmm_unpack_layout, "qmm_unpack_layout", Q_mfma, Q_canon, N, K, w_bit, stream)
 
 
-def _matmul(fn, x, Q, scales, zeros, y, M, N, K, w_bit, group_size, x_dtype, workspace,
+def _matmul_ptrs(name, x, Q, scales, zeros, y, y_size, y_dtypes, M, N, K, w_bit, group_size,
+                 workspace, workspace_bytes):
+    a = _Args(name)
+    xb, qb, sb, zb = _operand_bytes(M, N, K, w_bit, group_size)
+    yb = max(M, 0) * max(N, 0) * y_size
+    ptrs = (a(x, "x", xb, _F16S), a(Q, "Q", qb, _weight_dtypes(w_bit)),
+            a(scales, "scales", sb, _scale_dtypes(w_bit)), a(zeros, "zeros", zb, (torch.int32,)),
+            a(y, "y", yb, y_dtypes), a(workspace, "workspace", workspace_bytes))
+    return a, ptrs
+
+
+def _matmul(fn, name, x, Q, scales, zeros, y, M, N, K, w_bit, group_size, x_dtype, workspace,
             workspace_bytes, stream):
     if x_dtype is None:
         x_dtype = _dtype_code(x)
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(fn(_ptr(x), _ptr(Q), _ptr(scales), _ptr(zeros), _ptr(y), M, N, K, w_bit, group_size,
-              x_dtype, _ptr(workspace), workspace_bytes, _stream(stream)))
+    a, (px, pq, ps, pz, py, pw) = _matmul_ptrs(name, x, Q, scales, zeros, y, 4,
+                                               (torch.float32,), M, N, K, w_bit, group_size,
+                                               workspace, workspace_bytes)
+    _check(fn(px, pq, ps, pz, py, M, N, K, w_bit, group_size, x_dtype, pw, workspace_bytes,
+              a.stream(stream)))
 
 
 def qmm_gemv(x, Q, scales, zeros, y, M, N, K, w_bit, group_size, x_dtype=None,
              workspace=None, workspace_bytes=None, stream=None):
-    _matmul(_lib.qmm_gemv, x, Q, scales, zeros, y, M, N, K, w_bit, group_size, x_dtype,
-            workspace, workspace_bytes, stream)
+    _matmul(_lib.qmm_gemv, "qmm_gemv", x, Q, scales, zeros, y, M, N, K, w_bit, group_size,
+            x_dtype, workspace, workspace_bytes, stream)
 
 
 def qmm_gemm(x, Q, scales, zeros, y, M, N, K, w_bit, group_size, x_dtype=None,
              workspace=None, workspace_bytes=None, stream=None):
-    _matmul(_lib.qmm_gemm, x, Q, scales, zeros, y, M, N, K, w_bit, group_size, x_dtype,
-            workspace, workspace_bytes, stream)
+    _matmul(_lib.qmm_gemm, "qmm_gemm", x, Q, scales, zeros, y, M, N, K, w_bit, group_size,
+            x_dtype, workspace, workspace_bytes, stream)
 
 
 def _y_code(y):
@@ -148,7 +237,10 @@ def _y_code(y):
     raise QmmError(QMM_ERR_ARG, "y_dtype must be given when y is a raw pointer")
 
 
-def _matmul_ex(fn, x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit, group_size, x_dtype,
+_Y_SIZE = {QMM_F32: 4, QMM_F16: 2, QMM_BF16: 2}
+
+
+def _matmul_ex(fn, name, x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit, group_size, x_dtype,
                workspace, workspace_bytes, stream):
     if x_dtype is None:
         x_dtype = _dtype_code(x)
@@ -156,25 +248,35 @@ def _matmul_ex(fn, x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit, group_size, 
         y_dtype = _y_code(y)
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(fn(_ptr(x), _ptr(Q), _ptr(scales), _ptr(zeros), _ptr(y), y_dtype, M, N, K, w_bit,
-              group_size, x_dtype, _ptr(workspace), workspace_bytes, _stream(stream)))
+    y_dtypes = ({QMM_F32: (torch.float32,), QMM_F16: (torch.float16,),
+                 QMM_BF16: (torch.bfloat16,)}.get(y_dtype, _YS))
+    a, (px, pq, ps, pz, py, pw) = _matmul_ptrs(name, x, Q, scales, zeros, y,
+                                               _Y_SIZE.get(y_dtype, 0), y_dtypes, M, N, K,
+                                               w_bit, group_size, workspace, workspace_bytes)
+    _check(fn(px, pq, ps, pz, py, y_dtype, M, N, K, w_bit, group_size, x_dtype, pw,
+              workspace_bytes, a.stream(stream)))
 
 
 def qmm_gemv_ex(x, Q, scales, zeros, y, M, N, K, w_bit, group_size, y_dtype=None, x_dtype=None,
                 workspace=None, workspace_bytes=None, stream=None):
-    _matmul_ex(_lib.qmm_gemv_ex, x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit, group_size,
-               x_dtype, workspace, workspace_bytes, stream)
+    _matmul_ex(_lib.qmm_gemv_ex, "qmm_gemv_ex", x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit,
+               group_size, x_dtype, workspace, workspace_bytes, stream)
 
 
 def qmm_gemm_ex(x, Q, scales, zeros, y, M, N, K, w_bit, group_size, y_dtype=None, x_dtype=None,
                 workspace=None, workspace_bytes=None, stream=None):
-    _matmul_ex(_lib.qmm_gemm_ex, x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit, group_size,
-               x_dtype, workspace, workspace_bytes, stream)
+    _matmul_ex(_lib.qmm_gemm_ex, "qmm_gemm_ex", x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit,
+               group_size, x_dtype, workspace, workspace_bytes, stream)
 
 
 def qmm_dequant(Q, layout, scales, zeros, w_out, N, K, w_bit, group_size, stream=None):
-    _check(_lib.qmm_dequant(_ptr(Q), layout, _ptr(scales), _ptr(zeros), _ptr(w_out), N, K,
-                            w_bit, group_size, _stream(stream)))
+    a = _Args("qmm_dequant")
+    _, qb, sb, zb = _operand_bytes(1, N, K, w_bit, group_size)
+    ptrs = (a(Q, "Q", qb, _weight_dtypes(w_bit)), a(scales, "scales", sb, _scale_dtypes(w_bit)),
+            a(zeros, "zeros", zb, (torch.int32,)),
+            a(w_out, "w_out", max(N, 0) * max(K, 0) * 4, (torch.float32,)))
+    _check(_lib.qmm_dequant(ptrs[0], layout, ptrs[1], ptrs[2], ptrs[3], N, K, w_bit, group_size,
+                            a.stream(stream)))
 
 
 # ------------------------------------------------ tensor-level conveniences
@@ -183,7 +285,7 @@ _workspaces = {}
 
 def workspace_for(M, N, K, w_bit, group_size, device):
     """A zero-filled workspace large enough for (M, N, K), cached per device and
-    stream (the kernels leave it re-armed after every call)."""
+    stream, or None when the shape needs none."""
     need = qmm_workspace_bytes(M, N, K, w_bit, group_size)
     if need == 0:
         return None
@@ -240,16 +342,27 @@ def dequant(Q, layout, scales, zeros, N, K, w_bit, group_size):
 
 
 # ---------------------------------------- int8 x ternary (liger-kernel product)
+def _t2_layout(fn, name, src, dst, N, K, stream):
+    a = _Args(name)
+    nb = max(N, 0) * max(K, 0) // 4
+    ps, pd = a(src, "source", nb, _I8S), a(dst, "destination", nb, _I8S)
+    _check(fn(ps, pd, N, K, a.stream(stream)))
+
+
 def qmm_t2_pack(W_page, W_tile, N, K, stream=None):
-    _check(_lib.qmm_t2_pack(_ptr(W_page), _ptr(W_tile), N, K, _stream(stream)))
+    _t2_layout(_lib.qmm_t2_pack, "qmm_t2_pack", W_page, W_tile, N, K, stream)
 
 
 def qmm_t2_unpack_layout(W_tile, W_page, N, K, stream=None):
-    _check(_lib.qmm_t2_unpack_layout(_ptr(W_tile), _ptr(W_page), N, K, _stream(stream)))
+    _t2_layout(_lib.qmm_t2_unpack_layout, "qmm_t2_unpack_layout", W_tile, W_page, N, K, stream)
 
 
 def qmm_i8t2_gemm(x, W_tile, y, M, N, K, stream=None):
-    _check(_lib.qmm_i8t2_gemm(_ptr(x), _ptr(W_tile), _ptr(y), M, N, K, _stream(stream)))
+    a = _Args("qmm_i8t2_gemm")
+    M0, N0, K0 = max(M, 0), max(N, 0), max(K, 0)
+    ptrs = (a(x, "x", M0 * K0, _I8S), a(W_tile, "W_tile", N0 * K0 // 4, _I8S),
+            a(y, "y", M0 * N0 * 4, (torch.int32,)))
+    _check(_lib.qmm_i8t2_gemm(*ptrs, M, N, K, a.stream(stream)))
 
 
 def t2_pack(W_page, N, K):
@@ -269,8 +382,15 @@ def i8t2_gemm(x, W_tile, N, out=None):
 
 # ------------------------------------------------ round-to-nearest quantizer
 def qmm_quantize(W, w_dtype, qw, scales, qzeros, N, K, w_bit, group_size, symmetric, stream=None):
-    _check(_lib.qmm_quantize(_ptr(W), w_dtype, _ptr(qw), _ptr(scales), _ptr(qzeros), N, K, w_bit,
-                             group_size, int(symmetric), _stream(stream)))
+    a = _Args("qmm_quantize")
+    wdt = {QMM_F32: (torch.float32,), QMM_F16: (torch.float16,), QMM_BF16: (torch.bfloat16,)}
+    wsz = {QMM_F32: 4, QMM_F16: 2, QMM_BF16: 2}.get(w_dtype, 0)
+    _, qb, sb, zb = _operand_bytes(1, N, K, w_bit, group_size) if w_bit in (2, 4) else (0,) * 4
+    ptrs = (a(W, "W", max(N, 0) * max(K, 0) * wsz, wdt.get(w_dtype)),
+            a(qw, "qw", qb, (torch.int32,)), a(scales, "scales", sb, (torch.float16,)),
+            a(qzeros, "qzeros", 0 if symmetric else zb, (torch.int32,)))
+    _check(_lib.qmm_quantize(ptrs[0], w_dtype, ptrs[1], ptrs[2], ptrs[3], N, K, w_bit,
+                             group_size, int(symmetric), a.stream(stream)))
 
 
 def quantize(W, w_bit, group_size, symmetric=False):

@@ -399,7 +399,7 @@ template <> __device__ __forceinline__ void mfma16_acc<XBF16>(f32x4_t& c, const 
 // 16-row tiles per wave in the large-M kernel (rows per workgroup / 16):
 // 16 (one wave per SIMD, 256 accumulators) or 8 (two waves per SIMD).
 static int large_mt() {
-  const int e = env_int("QMM_LARGE_MT");
+  static const int e = env_int("QMM_LARGE_MT");
   return (e == 8 || e == 16) ? e : 16;
 }
 
@@ -770,14 +770,14 @@ static void skinny_shape(int M, int N, int* mt, int* nt) {
   // many workgroups as CUs (measured: 4 strips at N = 14336, 2 at N = 8192)
   const int strips = N / 16;
   *nt = strips / 4 >= 192 ? 4 : (strips / 2 >= 192 ? 2 : 1);
-  const int want = env_int("QMM_SKINNY_NT");
+  static const int want = env_int("QMM_SKINNY_NT");
   if (want == 1 || want == 2 || want == 4) *nt = want;
 }
 
 GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size) {
   GemmPlan p{};
   (void)group_size;
-  const int big = env_int("QMM_GEMM_LARGE_MIN_M");
+  static const int big = env_int("QMM_GEMM_LARGE_MIN_M");
   if (w_bit != 8 && M > (big > 0 ? big : 64) && K % 128 == 0) {
     p.kind = 1;
     p.mtile = 16 * large_mt();
@@ -806,7 +806,7 @@ GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size) {
   const int nst = (K + kb - 1) / kb;
   const bool w8 = nt == 1 && (mt == 1 || (mt == 2 && w_bit != 2));
   p.waves = (tiles < 128 && w8 && nst >= 16) ? 8 : 4;
-  const int want = env_int("QMM_SKINNY_WAVES");
+  static const int want = env_int("QMM_SKINNY_WAVES");
   if (want == 4 || (want == 8 && w8)) p.waves = want;
   p.workspace_bytes = 0;
   return p;
@@ -817,13 +817,10 @@ static hipError_t launch_skinny_w(const MatmulArgs& a, const GemmPlan& p) {
   // register budget: 4 waves per SIMD at 16 waves leave 128 registers a lane
   constexpr int DEPTH = MT >= 4 ? 2 : 3;
   const long blocks = (long)p.n_tiles * p.m_tiles;
-  hipLaunchKernelGGL((gemm_skinny_kernel<W_BIT, XDT, GS, MT, NT, DEPTH, WAVES>),
-                     dim3((unsigned)blocks), dim3(64 * WAVES), 0, a.stream,
-                     reinterpret_cast<const uint16_t*>(a.x),
-                     reinterpret_cast<const u32x4_t*>(a.Q), a.scales,
-                     reinterpret_cast<const uint32_t*>(a.zeros), a.y,
-                     a.M, a.N, a.K, pack_tiles(p.n_tiles, a.y_dtype, a.group_mask == 0));
-  return hipGetLastError();
+  return launch_kernel(gemm_skinny_kernel<W_BIT, XDT, GS, MT, NT, DEPTH, WAVES>,
+                       dim3((unsigned)blocks), dim3(64 * WAVES), a.stream, a.x, a.Q, a.scales,
+                       a.zeros, a.y, a.M, a.N, a.K,
+                       pack_tiles(p.n_tiles, a.y_dtype, a.group_mask == 0));
 }
 
 template <int W_BIT, int XDT, int GS, int MT, int NT>
@@ -872,13 +869,10 @@ static hipError_t launch_gs(const MatmulArgs& a, const GemmPlan& p) {
 
 template <int W_BIT, int XDT, int GS, bool ZP, int MT>
 static hipError_t launch_large_mt(const MatmulArgs& a, const GemmPlan& p) {
-  hipLaunchKernelGGL((gemm_large_kernel<W_BIT, XDT, GS, ZP, MT>), dim3((unsigned)(p.n_tiles * p.m_tiles)),
-                     dim3(256), 0, a.stream, reinterpret_cast<const uint16_t*>(a.x),
-                     reinterpret_cast<const u32x4_t*>(a.Q),
-                     reinterpret_cast<const uint16_t*>(a.scales),
-                     reinterpret_cast<const uint32_t*>(a.zeros), a.y,
-                     a.M, a.N, a.K, pack_tiles(p.n_tiles, a.y_dtype, a.group_mask == 0));
-  return hipGetLastError();
+  return launch_kernel(gemm_large_kernel<W_BIT, XDT, GS, ZP, MT>,
+                       dim3((unsigned)(p.n_tiles * p.m_tiles)), dim3(256), a.stream, a.x, a.Q,
+                       a.scales, a.zeros, a.y, a.M, a.N, a.K,
+                       pack_tiles(p.n_tiles, a.y_dtype, a.group_mask == 0));
 }
 
 template <int W_BIT, int XDT, int GS, bool ZP>

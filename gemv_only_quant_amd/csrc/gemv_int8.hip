@@ -120,7 +120,7 @@ GemvInt8Plan plan_gemv_int8(int M, int N, int K) {
   p.mb = m_bucket8(M);
   // enough waves to cover the chip; more rows per wave once N is large
   int rn = (N >= 8192 && M <= 4) ? 4 : (N >= 4096 ? 2 : 1);
-  const int want = env_int("QMM_GEMV8_RN");
+  static const int want = env_int("QMM_GEMV8_RN");
   if (want == 1 || want == 2 || want == 4) rn = want;
   p.rn = rn;
   const int waves = (N + rn - 1) / rn;
@@ -136,12 +136,11 @@ static hipError_t launch8(const MatmulArgs& a, const GemvInt8Plan& p) {
   auto Q = reinterpret_cast<const int8_t*>(a.Q);
   auto s = reinterpret_cast<const float*>(a.scales);
   switch (p.rn) {
-    case 1: hipLaunchKernelGGL((gemv_int8_kernel<XDT, MB, 1>), grid, block, 0, a.stream, xq, Q, s, a.y, a.y_dtype, a.M, a.N, a.K); break;
-    case 2: hipLaunchKernelGGL((gemv_int8_kernel<XDT, MB, 2>), grid, block, 0, a.stream, xq, Q, s, a.y, a.y_dtype, a.M, a.N, a.K); break;
-    case 4: hipLaunchKernelGGL((gemv_int8_kernel<XDT, MB, 4>), grid, block, 0, a.stream, xq, Q, s, a.y, a.y_dtype, a.M, a.N, a.K); break;
-    default: return hipErrorInvalidValue;
+    case 1: return launch_kernel(gemv_int8_kernel<XDT, MB, 1>, grid, block, a.stream, xq, Q, s, a.y, a.y_dtype, a.M, a.N, a.K);
+    case 2: return launch_kernel(gemv_int8_kernel<XDT, MB, 2>, grid, block, a.stream, xq, Q, s, a.y, a.y_dtype, a.M, a.N, a.K);
+    case 4: return launch_kernel(gemv_int8_kernel<XDT, MB, 4>, grid, block, a.stream, xq, Q, s, a.y, a.y_dtype, a.M, a.N, a.K);
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 template <int XDT>

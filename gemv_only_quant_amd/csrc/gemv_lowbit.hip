@@ -257,7 +257,7 @@ GemvLowbitPlan plan_gemv_lowbit(int M, int N, int K, int w_bit, int group_size) 
   while (rl > 2 && (rl > rpg || rpg % rl != 0)) rl /= 2;
   while (rl > 2 && rl * 64 / 2 >= rows) rl /= 2;
   while (rl > 2 && x_lds_bytes(p.mb, rl, pairs) > kXldsMax) rl /= 2;
-  const int want = env_int("QMM_GEMV_RL");
+  static const int want = env_int("QMM_GEMV_RL");
   if (want >= 2 && want <= rl && (rl % want) == 0) rl = want;
   p.rl = rl;
   p.workspace_bytes = 0;
@@ -271,12 +271,9 @@ static hipError_t launch_rl(const MatmulArgs& a, const GemvLowbitPlan& p) {
   } else {
   const auto k = a.y_dtype == YF32 ? gemv_lowbit_kernel<W_BIT, XDT, MB, RL, 4, 4, true>
                                    : gemv_lowbit_kernel<W_BIT, XDT, MB, RL, 4, 4, false>;
-  hipLaunchKernelGGL(k, dim3(p.n_tiles), dim3(256), 0, a.stream,
-                     reinterpret_cast<const uint16_t*>(a.x), reinterpret_cast<const uint32_t*>(a.Q),
-                     reinterpret_cast<const uint16_t*>(a.scales),
-                     reinterpret_cast<const uint32_t*>(a.zeros), a.y,
-                     a.y_dtype == YF32 ? a.M : (a.M | (a.y_dtype << 8)), a.N, a.K, a.group_size);
-  return hipGetLastError();
+  return launch_kernel(k, dim3(p.n_tiles), dim3(256), a.stream, a.x, a.Q, a.scales, a.zeros, a.y,
+                       a.y_dtype == YF32 ? a.M : (a.M | (a.y_dtype << 8)), a.N, a.K,
+                       a.group_size);
   }
 }
 

@@ -4,7 +4,25 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 namespace qmm {
+
+// Launches kernel `k` on `s` and returns the status of this launch alone: an
+// error that an earlier call left on the thread is neither reported nor
+// cleared.  The arguments are converted to the kernel's parameter types.
+template <typename... P, typename... A>
+hipError_t launch_kernel(void (*k)(P...), dim3 grid, dim3 block, hipStream_t s, A&&... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<P...> v(static_cast<P>(std::forward<A>(args))...);
+  return std::apply(
+      [&](auto&... e) {
+        void* p[] = {static_cast<void*>(&e)...};
+        return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, p, 0, s);
+      },
+      v);
+}
 
 // Arguments shared by every matmul launcher, already validated.
 struct MatmulArgs {
@@ -74,6 +92,8 @@ hipError_t launch_quantize(const void* W, int w_dtype, void* qw, void* scales, v
                            int N, int K, int w_bit, int group_size, int symmetric, hipStream_t s);
 
 // Optional integer override from the environment (tile sweeps); -1 if unset.
+// Call sites keep the value in a function-local static, so each override is
+// read once per process, at the first call that plans that kernel.
 int env_int(const char* name);
 
 }  // namespace qmm

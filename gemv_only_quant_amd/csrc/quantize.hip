@@ -144,19 +144,20 @@ hipError_t launch_quantize(const void* W, int w_dtype, void* qw, void* scales, v
   auto* z = reinterpret_cast<uint32_t*>(qzeros);
   auto go = [&](auto bits, auto wdt) {
     constexpr int B = decltype(bits)::value, D = decltype(wdt)::value;
-    hipLaunchKernelGGL((rtn_scales_kernel<B, D>), dim3((unsigned)blocks1), dim3(64 * (32 / B)), 0,
-                       st, W, s, z, N, K, group_size, symmetric);
-    hipLaunchKernelGGL((rtn_codes_kernel<B, D>), dim3((unsigned)blocks2), dim3(256), 0, st, W, s,
-                       z, q, N, K, group_size, symmetric);
+    const hipError_t e = launch_kernel(rtn_scales_kernel<B, D>, dim3((unsigned)blocks1),
+                                       dim3(64 * (32 / B)), st, W, s, z, N, K, group_size,
+                                       symmetric);
+    if (e != hipSuccess) return e;
+    return launch_kernel(rtn_codes_kernel<B, D>, dim3((unsigned)blocks2), dim3(256), st, W, s, z,
+                         q, N, K, group_size, symmetric);
   };
   auto by_dtype = [&](auto bits) {
-    if (w_dtype == YF32) go(bits, std::integral_constant<int, YF32>{});
-    else if (w_dtype == XF16) go(bits, std::integral_constant<int, XF16>{});
-    else go(bits, std::integral_constant<int, XBF16>{});
+    if (w_dtype == YF32) return go(bits, std::integral_constant<int, YF32>{});
+    if (w_dtype == XF16) return go(bits, std::integral_constant<int, XF16>{});
+    return go(bits, std::integral_constant<int, XBF16>{});
   };
-  if (w_bit == 4) by_dtype(std::integral_constant<int, 4>{});
-  else by_dtype(std::integral_constant<int, 2>{});
-  return hipGetLastError();
+  if (w_bit == 4) return by_dtype(std::integral_constant<int, 4>{});
+  return by_dtype(std::integral_constant<int, 2>{});
 }
 
 }  // namespace qmm

@@ -144,33 +144,27 @@ static unsigned blocks_for(size_t n, int t) { return (unsigned)((n + t - 1) / t)
 hipError_t launch_pack(const void* q_canon, void* q_mfma, int N, int K, int w_bit,
                        hipStream_t st) {
   const int T = 256;
-  if (w_bit == 4) {
-    hipLaunchKernelGGL(pack4_kernel, dim3(blocks_for((size_t)N * K / 8, T)), dim3(T), 0, st,
-                       (const uint32_t*)q_canon, (uint32_t*)q_mfma, N, K);
-  } else if (w_bit == 2) {
-    hipLaunchKernelGGL(pack2_kernel, dim3(blocks_for((size_t)N * K / 16, T)), dim3(T), 0, st,
-                       (const uint32_t*)q_canon, (uint32_t*)q_mfma, N, K);
-  } else {
-    hipLaunchKernelGGL(pack8_kernel, dim3(blocks_for((size_t)N * K / 16, T)), dim3(T), 0, st,
-                       (const uint8_t*)q_canon, (uint8_t*)q_mfma, N, K);
-  }
-  return hipGetLastError();
+  if (w_bit == 4)
+    return launch_kernel(pack4_kernel, dim3(blocks_for((size_t)N * K / 8, T)), dim3(T), st, q_canon,
+                         q_mfma, N, K);
+  if (w_bit == 2)
+    return launch_kernel(pack2_kernel, dim3(blocks_for((size_t)N * K / 16, T)), dim3(T), st, q_canon,
+                         q_mfma, N, K);
+  return launch_kernel(pack8_kernel, dim3(blocks_for((size_t)N * K / 16, T)), dim3(T), st, q_canon,
+                       q_mfma, N, K);
 }
 
 hipError_t launch_unpack_layout(const void* q_mfma, void* q_canon, int N, int K, int w_bit,
                                 hipStream_t st) {
   const int T = 256;
-  if (w_bit == 4) {
-    hipLaunchKernelGGL(unpack4_kernel, dim3(blocks_for((size_t)N * K / 8, T)), dim3(T), 0, st,
-                       (const uint32_t*)q_mfma, (uint32_t*)q_canon, N, K);
-  } else if (w_bit == 2) {
-    hipLaunchKernelGGL(unpack2_kernel, dim3(blocks_for((size_t)N * K / 16, T)), dim3(T), 0, st,
-                       (const uint32_t*)q_mfma, (uint32_t*)q_canon, N, K);
-  } else {
-    hipLaunchKernelGGL(unpack8_kernel, dim3(blocks_for((size_t)N * K / 8, T)), dim3(T), 0, st,
-                       (const uint8_t*)q_mfma, (uint8_t*)q_canon, N, K);
-  }
-  return hipGetLastError();
+  if (w_bit == 4)
+    return launch_kernel(unpack4_kernel, dim3(blocks_for((size_t)N * K / 8, T)), dim3(T), st, q_mfma,
+                         q_canon, N, K);
+  if (w_bit == 2)
+    return launch_kernel(unpack2_kernel, dim3(blocks_for((size_t)N * K / 16, T)), dim3(T), st, q_mfma,
+                         q_canon, N, K);
+  return launch_kernel(unpack8_kernel, dim3(blocks_for((size_t)N * K / 8, T)), dim3(T), st, q_mfma,
+                       q_canon, N, K);
 }
 
 // --- dequant export ----------------------------------------------------------
@@ -228,10 +222,8 @@ __global__ void dequant_kernel(const void* __restrict__ Q, int layout,
 hipError_t launch_dequant(const void* Q, int layout, const void* scales, const void* zeros,
                           float* w, int N, int K, int w_bit, int group_size, hipStream_t st) {
   const int T = 256;
-  hipLaunchKernelGGL(dequant_kernel, dim3(blocks_for((size_t)N * K, T)), dim3(T), 0, st, Q,
-                     layout, (const uint16_t*)scales, (const uint32_t*)zeros, w, N, K, w_bit,
-                     group_size);
-  return hipGetLastError();
+  return launch_kernel(dequant_kernel, dim3(blocks_for((size_t)N * K, T)), dim3(T), st, Q, layout,
+                       scales, zeros, w, N, K, w_bit, group_size);
 }
 
 }  // namespace qmm

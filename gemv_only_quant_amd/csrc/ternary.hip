@@ -351,16 +351,14 @@ __global__ __launch_bounds__(256) void i8t2_skinny_kernel(const int8_t* __restri
 // ---------------------------------------------------------------- host side
 hipError_t launch_t2_pack(const void* Wp, void* Wt, int N, int K, hipStream_t st) {
   const size_t total = (size_t)N * K / 16;
-  hipLaunchKernelGGL(t2_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                     reinterpret_cast<const uint8_t*>(Wp), reinterpret_cast<uint32_t*>(Wt), N, K);
-  return hipGetLastError();
+  return launch_kernel(t2_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), st, Wp, Wt,
+                       N, K);
 }
 
 hipError_t launch_t2_unpack(const void* Wt, void* Wp, int N, int K, hipStream_t st) {
   const size_t total = (size_t)N * K / 4;
-  hipLaunchKernelGGL(t2_unpack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
-                     reinterpret_cast<const uint32_t*>(Wt), reinterpret_cast<uint8_t*>(Wp), N, K);
-  return hipGetLastError();
+  return launch_kernel(t2_unpack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), st, Wt,
+                       Wp, N, K);
 }
 
 template <int MT, int NT4>
@@ -369,10 +367,8 @@ static hipError_t launch_i8t2(const void* x, const void* Wt, int32_t* y, int M, 
   const int strips = N / 16;
   const int n_tiles = (strips + 4 * NT4 - 1) / (4 * NT4);
   const int m_tiles = (M + 16 * MT - 1) / (16 * MT);
-  hipLaunchKernelGGL((i8t2_gemm_kernel<MT, NT4>), dim3((unsigned)(n_tiles * m_tiles)), dim3(256), 0,
-                     st, reinterpret_cast<const int8_t*>(x), reinterpret_cast<const u32x4_t*>(Wt),
-                     y, M, N, K, n_tiles);
-  return hipGetLastError();
+  return launch_kernel(i8t2_gemm_kernel<MT, NT4>, dim3((unsigned)(n_tiles * m_tiles)), dim3(256),
+                       st, x, Wt, y, M, N, K, n_tiles);
 }
 
 hipError_t launch_i8t2_gemm(const void* x, const void* Wt, int32_t* y, int M, int N, int K,
@@ -380,10 +376,8 @@ hipError_t launch_i8t2_gemm(const void* x, const void* Wt, int32_t* y, int M, in
   if (M <= 16) {
     // one strip per workgroup; K split over its 4 waves
     const int n_tiles = N / 16;
-    hipLaunchKernelGGL((i8t2_skinny_kernel<1>), dim3((unsigned)n_tiles), dim3(256), 0, st,
-                       reinterpret_cast<const int8_t*>(x), reinterpret_cast<const u32x4_t*>(Wt), y,
-                       M, N, K, n_tiles);
-    return hipGetLastError();
+    return launch_kernel(i8t2_skinny_kernel<1>, dim3((unsigned)n_tiles), dim3(256), st, x, Wt, y,
+                         M, N, K, n_tiles);
   }
   if (M <= 64) return launch_i8t2<1, 1>(x, Wt, y, M, N, K, st);
   return launch_i8t2<8, 4>(x, Wt, y, M, N, K, st);

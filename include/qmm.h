@@ -11,10 +11,11 @@
  *  - operands and the canonical packed layout: BitDistiller,
  *    quantization/triton_kernels.py, quant_matmul_kernel (docstring shapes
  *    a (M,K), qw (K/pack_num, N), scales (K/group_size, N),
- *    qzeros (K/group_size/pack_num, N); unpack "(qw >> (k % pack_num) *
- *    w_bit) & offset"; group index floor(k / group_size));
+ *    qzeros (K/group_size/pack_num, N); the unpack shifts the word right by
+ *    (k mod pack_num) * w_bit and masks with offset; group index
+ *    floor(k / group_size));
  *  - the symmetric int4 zero point 8: aphrodite-engine marlin_cuda_kernel.cu,
- *    dequant() ("-8 symmetric zero point");
+ *    dequant() (the zero point 8 folded into its int4 conversion constants);
  *  - int8 weights (N, K) with the fp32 row scale applied after an fp32 sum:
  *    tiny-llm src/tinyllm/kernels/int8_gemv.py (module and int8_matmul
  *    docstrings);
@@ -94,7 +95,11 @@ QMM_API int qmm_version(void);
 QMM_API const char* qmm_last_error(void);
 
 /* Bytes of Q for an (N, K) weight in `layout`; 0 if the combination is
- * invalid.  Both layouts hold N*K*w_bit/8 bytes. */
+ * invalid.  Both layouts hold N*K*w_bit/8 bytes: the canonical low-bit
+ * weight is BitDistiller quant_matmul_kernel's qw, (K/pack_num, N) int32
+ * (its docstring shapes); int8 is tiny-llm int8_gemv.py's q, (N, K) int8
+ * (int8_matmul docstring); the tile layout (qmm_pack) is a permutation of
+ * the same bits. */
 QMM_API size_t qmm_packed_bytes(int N, int K, int w_bit, int layout);
 
 /*
@@ -140,8 +145,15 @@ QMM_API qmm_status qmm_gemv(const void* x, const void* Q, const void* scales, co
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * qmm_gemm: any M >= 1, Q in the MFMA layout produced by qmm_pack
- * (N % 16 == 0, K % KB == 0).  Contraction on the matrix cores.
+ * qmm_gemm: the same product as qmm_gemv for any M >= 1, Q in the MFMA
+ * layout produced by qmm_pack (N % 16 == 0, K % KB == 0), contracted on the
+ * matrix cores.  The operation is BitDistiller quant_matmul_kernel's
+ * a (M,K) times dequant(qw) accumulated in fp32 (int8: tiny-llm's
+ * y = scale * (x . q) with the scale after the sum); that larger batches are
+ * a dense contraction for the matrix units is tiny-llm int8_gemv.py's note
+ * on MAX_M (past a few rows the product is a plain GEMM) and the premise of Marlin's
+ * tensor-core kernel (aphrodite-engine marlin_cuda_kernel.cu, Marlin<...>).
+ * Output and errors as qmm_gemv; M > 16 is allowed.
  */
 QMM_API qmm_status qmm_gemm(const void* x, const void* Q, const void* scales, const void* zeros,
                     float* y, int M, int N, int K, int w_bit, int group_size, int x_dtype,
@@ -167,6 +179,12 @@ QMM_API qmm_status qmm_gemm_ex(const void* x, const void* Q, const void* scales,
  * qmm_dequant: W (K, N) fp32 from Q in either layout, bit-exact:
  * W[k][n] = float(q - z) * float(s) for low-bit (exact in fp32), and
  * W[k][n] = float(Q[n][k]) for int8 (row scale NOT applied).  For tests.
+ * The codes, group index and zero unpacking are BitDistiller
+ * quant_matmul_kernel's ((qw >> shift) & offset, group floor(k/group_size));
+ * (q - z) * s with an integer zero in code space is aphrodite-engine
+ * marlin_cuda_kernel.cu dequant()'s symmetric (q - 8) * s with z read from
+ * qzeros (the BitDistiller page is cut off before its own dequant line).
+ * w_out is (K, N) fp32, fully overwritten; errors as qmm_gemv.
  */
 QMM_API qmm_status qmm_dequant(const void* Q, int layout, const void* scales, const void* zeros,
                        float* w_out, int N, int K, int w_bit, int group_size, void* stream);
@@ -177,7 +195,7 @@ QMM_API qmm_status qmm_dequant(const void* Q, int layout, const void* scales, co
  * values in {-1, 0, +1}, exact.  The page stores W as pack_weights does:
  * (K/4, N) uint8, K split into four consecutive quarters of R = K/4 rows,
  * quarter i in bits 2i..2i+1, each field the value + 1 (code 3 reads as +2,
- * as unpack_weights's "mask, shift, minus 1" gives).
+ * as unpack_weights gives: it masks the field, shifts it down and subtracts 1).
  *
  * qmm_t2_pack rewrites that once into the tile layout qmm_i8t2_gemm reads:
  * 1 KiB blocks, one per (16-column strip s, 256-deep K block kb),

@@ -186,21 +186,21 @@ def test_gemm_large_one_hot_reproduces_weights():
 
 
 # ------------------------------------ small N, long K: 8 waves split K per tile
-MANYWAVES = [  # M, N, K, w_bit, group, x_dtype, symmetric, forced waves (0 = planner's)
-    (16, 64, 4096, 4, 128, si.F16, False, 0),      # 4 tiles, 32 stages -> 8 waves
-    (3, 256, 8192, 4, 64, si.BF16, False, 0),      # ragged M
-    (1, 32, 6144, 4, 256, si.F16, True, 0),        # 48 stages: uneven shares
-    (16, 80, 5120, 4, 32, si.BF16, False, 8),      # 40 stages over 8 waves, g32
-    (30, 48, 4096, 4, 128, si.F16, False, 0),      # two 16-row tiles -> 8 waves
-    (16, 48, 8192, 2, 64, si.BF16, False, 0),      # int2 -> 8 waves
-    (9, 16, 1152, 4, 128, si.BF16, False, 8),      # 9 stages: waves 5..7 idle
+# Shapes whose tiles alone leave most CUs idle (< 128 tiles, >= 16 stages of
+# K): the planner gives each workgroup 8 waves that split K.
+MANYWAVES = [  # M, N, K, w_bit, group, x_dtype, symmetric
+    (16, 64, 4096, 4, 128, si.F16, False),      # 4 tiles, 32 stages
+    (3, 256, 8192, 4, 64, si.BF16, False),      # ragged M
+    (1, 32, 6144, 4, 256, si.F16, True),        # 48 stages: uneven shares
+    (16, 80, 5120, 4, 32, si.BF16, False),      # 40 stages over 8 waves, g32
+    (30, 48, 4096, 4, 128, si.F16, False),      # two 16-row tiles
+    (16, 48, 8192, 2, 64, si.BF16, False),      # int2
+    (9, 16, 2176, 4, 128, si.BF16, False),      # 17 stages: 3 per wave, waves 6 and 7 idle
 ]
 
 
-@pytest.mark.parametrize("M,N,K,w_bit,gs,xdt,sym,waves", MANYWAVES)
-def test_gemm_many_waves_within_bound(M, N, K, w_bit, gs, xdt, sym, waves, monkeypatch):
-    if waves:
-        monkeypatch.setenv("QMM_SKINNY_WAVES", str(waves))
+@pytest.mark.parametrize("M,N,K,w_bit,gs,xdt,sym", MANYWAVES)
+def test_gemm_many_waves_within_bound(M, N, K, w_bit, gs, xdt, sym):
     case = si.lowbit_case(M, N, K, w_bit, gs, xdt, sym, seed=900 + M + N + K)
     y = run_gemm(case)
     y_ref, a_ref = oracle.qmm(*case.oracle_args())
@@ -215,11 +215,9 @@ def test_gemm_many_waves_int8_within_bound(M, N, K, xdt):
     assert_within_bound(y, y_ref, a_ref, f"waves int8 M{M} N{N} K{K}")
 
 
-@pytest.mark.parametrize("M,N,K,w_bit,gs,waves", [(16, 64, 4096, 4, 128, 8),
-                                                  (5, 32, 8192, 2, 64, 8),
-                                                  (20, 16, 4096, 4, 64, 8)])
-def test_gemm_many_waves_exact_probe_bit_exact(M, N, K, w_bit, gs, waves, monkeypatch):
-    monkeypatch.setenv("QMM_SKINNY_WAVES", str(waves))
+@pytest.mark.parametrize("M,N,K,w_bit,gs", [(16, 64, 4096, 4, 128), (5, 32, 8192, 2, 64),
+                                             (20, 16, 4096, 4, 64)])
+def test_gemm_many_waves_exact_probe_bit_exact(M, N, K, w_bit, gs):
     case = si.exact_lowbit_case(M, N, K, w_bit, gs, si.BF16, False, seed=M + N)
     y = run_gemm(case)
     y_ref, _ = oracle.qmm(*case.oracle_args())
