@@ -87,11 +87,15 @@ __device__ __forceinline__ u32x4_t bfrag(const u32x4_t* slot, int st) {
   return b;
 }
 
-template <int W_BIT, int XDT, int GS, int MT, int NT, int DEPTH, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
+// SPLIT: K is also divided over S = splits_of(tile_opts) workgroups per tile
+// (consecutive work ids, so one XCD); each writes its partial tile to the
+// workspace and takes a ticket, and the last of the S to arrive adds the S
+// partials in split order and writes y (see the end of the body).
+template <int W_BIT, int XDT, int GS, int MT, int NT, int DEPTH, int WAVES, bool SPLIT>
+__device__ __forceinline__ void skinny_body(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ Qt,
     const void* __restrict__ scales, const uint32_t* __restrict__ qz, void* __restrict__ y,
-    int M, int N, int K, int tile_opts) {
+    uint32_t* __restrict__ ws, int M, int N, int K, int tile_opts) {
   const int n_tiles = tiles_of(tile_opts), ydt = ydt_of(tile_opts), gmask = gmask_of(tile_opts);
   constexpr int KB = Stage<W_BIT>::KB;
   constexpr int BLK = Stage<W_BIT>::BLK;
@@ -110,17 +114,22 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
   // run under an exec mask with its ring registers reused as temporaries)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, quad = lane >> 4;
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int S = SPLIT ? splits_of(tile_opts) : 1;
+  const int w0 = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = SPLIT ? w0 % S : 0;
+  const int w = SPLIT ? w0 / S : w0;  // tile
   const int nt = w % n_tiles, mt_idx = w / n_tiles;
   const int m0 = mt_idx * 16 * MT;
   const int strips = N / 16;
   const int s0 = nt * NT;
   const int nblk = K / KB;
   const int nst = (nblk + BLK - 1) / BLK;  // stages along K
-  // this wave's share of the stages
-  const int per = (nst + WAVES - 1) / WAVES;
-  const int st0 = min(nst, wave * per);
-  const int st1 = min(nst, st0 + per);
+  // this workgroup's split of the stages, then this wave's share of it
+  const int sper = (nst + S - 1) / S;
+  const int sp0 = min(nst, split * sper), sp1 = min(nst, sp0 + sper);
+  const int per = (sp1 - sp0 + WAVES - 1) / WAVES;
+  const int st0 = min(sp1, sp0 + wave * per);
+  const int st1 = min(sp1, st0 + per);
 
   // x of a stage arrives as whole rows (CH 16-byte chunks of a row per
   // stage, 64 / CH rows per load: a fragment-order load would touch 16 rows
@@ -306,19 +315,90 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) red[wave][16 * i + 4 * quad + r][16 * s + l16] = yacc[i][s][r];
   __syncthreads();
-  with_y(y, ydt, [&](auto* yt) {
-    using T = typename std::remove_pointer<decltype(yt)>::type;
-    for (int o = threadIdx.x; o < ROWS * COLS; o += 64 * WAVES) {
-      const int rr = o / COLS, cc = o % COLS;
-      const int m = m0 + rr, n = 16 * s0 + cc;
-      if (m < M && n < N) {
+  if constexpr (!SPLIT) {
+    with_y(y, ydt, [&](auto* yt) {
+      using T = typename std::remove_pointer<decltype(yt)>::type;
+      for (int o = threadIdx.x; o < ROWS * COLS; o += 64 * WAVES) {
+        const int rr = o / COLS, cc = o % COLS;
+        const int m = m0 + rr, n = 16 * s0 + cc;
+        if (m < M && n < N) {
+          float sum = 0.f;
+#pragma unroll
+          for (int v = 0; v < WAVES; ++v) sum += red[v][rr][cc];
+          yt[(size_t)m * N + n] = (T)sum;
+        }
+      }
+    });
+  } else {
+    // Workspace: one ticket per tile (zero between calls), padded to 256
+    // bytes, then S partial tiles of ROWS x COLS fp32 per tile.  The partial
+    // goes out with coherent stores; once they have completed (vmcnt 0 in
+    // every wave, then the barrier) one lane takes the tile's ticket.  The
+    // ticket is an agent-scope atomic, so whichever workgroup draws S - 1 is
+    // the last, and every other partial of its tile is already past the L2s;
+    // it re-arms the ticket and reads the S partials back with coherent
+    // loads.  Nobody waits on anybody: the workgroups that are not last end.
+    const int tiles = gridDim.x / S;
+    uint32_t* tickets = ws;
+    float* parts = reinterpret_cast<float*>(ws + ((tiles + 63) & ~63));
+    constexpr int PART = ROWS * COLS;  // floats per partial
+    const buf_t pbuf = make_buf(parts + (size_t)w * S * PART, (uint32_t)S * PART * 4u);
+    for (int o = 4 * threadIdx.x; o < PART; o += 4 * 64 * WAVES) {
+      const int rr = o / COLS, cc = o % COLS;  // 4 columns of one row (COLS % 16 == 0)
+      u32x4_t v;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
         float sum = 0.f;
 #pragma unroll
-        for (int v = 0; v < WAVES; ++v) sum += red[v][rr][cc];
-        yt[(size_t)m * N + n] = (T)sum;
+        for (int q = 0; q < WAVES; ++q) sum += red[q][rr][cc + c];
+        v[c] = __builtin_bit_cast(uint32_t, sum);
       }
+      buf_store128_coherent(v, pbuf, (split * PART + o) * 4);
     }
-  });
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __shared__ int last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t ticket =
+          __hip_atomic_fetch_add(tickets + w, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last = ticket == (uint32_t)(S - 1);
+      if (last) __hip_atomic_store(tickets + w, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!last) return;
+    with_y(y, ydt, [&](auto* yt) {
+      using T = typename std::remove_pointer<decltype(yt)>::type;
+      for (int o = 4 * threadIdx.x; o < PART; o += 4 * 64 * WAVES) {
+        f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < S; ++q)
+          sum += __builtin_bit_cast(f32x4_t, buf_load128_coherent(pbuf, (q * PART + o) * 4));
+        const int rr = o / COLS, cc = o % COLS;
+        const int m = m0 + rr, n = 16 * s0 + cc;
+        if (m < M && n < N) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) yt[(size_t)m * N + n + c] = (T)sum[c];
+        }
+      }
+    });
+  }
+}
+
+template <int W_BIT, int XDT, int GS, int MT, int NT, int DEPTH, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemm_skinny_kernel(
+    const uint16_t* __restrict__ x, const u32x4_t* __restrict__ Qt,
+    const void* __restrict__ scales, const uint32_t* __restrict__ qz, void* __restrict__ y,
+    int M, int N, int K, int tile_opts) {
+  skinny_body<W_BIT, XDT, GS, MT, NT, DEPTH, WAVES, false>(x, Qt, scales, qz, y, nullptr, M, N,
+                                                           K, tile_opts);
+}
+
+template <int W_BIT, int XDT, int GS, int MT, int NT, int DEPTH, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemm_skinny_split_kernel(
+    const uint16_t* __restrict__ x, const u32x4_t* __restrict__ Qt,
+    const void* __restrict__ scales, const uint32_t* __restrict__ qz, void* __restrict__ y,
+    uint32_t* __restrict__ ws, int M, int N, int K, int tile_opts) {
+  skinny_body<W_BIT, XDT, GS, MT, NT, DEPTH, WAVES, true>(x, Qt, scales, qz, y, ws, M, N, K,
+                                                          tile_opts);
 }
 
 // ---------------------------------------------------------------------------
@@ -774,7 +854,7 @@ static void skinny_shape(int M, int N, int* mt, int* nt) {
   if (want == 1 || want == 2 || want == 4) *nt = want;
 }
 
-GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size) {
+GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size, bool with_workspace) {
   GemmPlan p{};
   (void)group_size;
   static const int big = env_int("QMM_GEMM_LARGE_MIN_M");
@@ -785,6 +865,7 @@ GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size) {
     p.m_tiles = (M + p.mtile - 1) / p.mtile;
     p.nt = 16;
     p.waves = 4;
+    p.splits = 1;
     p.workspace_bytes = 0;
     return p;
   }
@@ -795,20 +876,37 @@ GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size) {
   p.n_tiles = (N / 16 + nt - 1) / nt;
   p.m_tiles = (M + p.mtile - 1) / p.mtile;
   p.nt = nt;
-  // Few tiles (small N) leave most CUs idle: 8 waves per workgroup put
-  // twice as much of K in flight, and their partial sums still meet in LDS.
-  // (Measured at M=16, K=14336, N=1024: 4 waves 19.6 us, 8 waves 18.2, 16
-  // waves 21.0; splitting K over workgroups instead, with arrival tickets,
-  // 24-47 us -- its agent-scope fences write back and invalidate the XCD's
-  // L2.)  Every wave keeps >= 2 stages.
   const long tiles = (long)p.n_tiles * p.m_tiles;
   const int kb = w_bit == 8 ? 128 : mfma_kblock(w_bit);
   const int nst = (K + kb - 1) / kb;
+  // Few tiles (small N, long K) leave most CUs idle.  With a workspace, K is
+  // split over S workgroups per tile (the last to arrive adds the partials),
+  // as many as one round of workgroups holds (tiles * S <= 256), each wave
+  // keeping >= 2 stages, and at most 4: every split adds a serial chain to
+  // the tile's end (its partial written through to memory, the ticket, the
+  // partials read back).  Measured at M=16, K=14336, N=1024 (64 tiles): S = 1
+  // 13.4 us, 2 10.4, 3 9.3, 4 9.1, 6 10.6, 8 11.5; at 224 tiles (int8,
+  // N=14336) S = 2 is 1.3x slower than none.  Without a workspace, 8 waves
+  // per workgroup put twice as much of K in flight and their partial sums
+  // still meet in LDS.
+  p.splits = 1;
+  static const int want_s = env_int("QMM_SKINNY_SPLITS");
+  if (with_workspace && tiles <= 128) {
+    int s = (int)(256 / tiles);
+    if (s > 4) s = 4;
+    while (s > 1 && nst / s < 8) --s;  // 4 waves x 2 stages
+    p.splits = s;
+  }
+  if (with_workspace && want_s >= 1 && want_s <= 16) p.splits = want_s;
   const bool w8 = nt == 1 && (mt == 1 || (mt == 2 && w_bit != 2));
-  p.waves = (tiles < 128 && w8 && nst >= 16) ? 8 : 4;
+  p.waves = (p.splits == 1 && tiles < 128 && w8 && nst >= 16) ? 8 : 4;
   static const int want = env_int("QMM_SKINNY_WAVES");
-  if (want == 4 || (want == 8 && w8)) p.waves = want;
+  if (p.splits == 1 && (want == 4 || (want == 8 && w8))) p.waves = want;
   p.workspace_bytes = 0;
+  if (p.splits > 1) {
+    const size_t tickets = (size_t)((tiles + 63) & ~63L) * 4;
+    p.workspace_bytes = tickets + (size_t)tiles * p.splits * p.mtile * 16 * nt * 4;
+  }
   return p;
 }
 
@@ -817,6 +915,13 @@ static hipError_t launch_skinny_w(const MatmulArgs& a, const GemmPlan& p) {
   // register budget: 4 waves per SIMD at 16 waves leave 128 registers a lane
   constexpr int DEPTH = MT >= 4 ? 2 : 3;
   const long blocks = (long)p.n_tiles * p.m_tiles;
+  if constexpr (WAVES == 4) {
+    if (p.splits > 1)
+      return launch_kernel(gemm_skinny_split_kernel<W_BIT, XDT, GS, MT, NT, DEPTH, WAVES>,
+                           dim3((unsigned)(blocks * p.splits)), dim3(64 * WAVES), a.stream, a.x,
+                           a.Q, a.scales, a.zeros, a.y, a.workspace, a.M, a.N, a.K,
+                           pack_tiles(p.n_tiles, a.y_dtype, a.group_mask == 0, p.splits));
+  }
   return launch_kernel(gemm_skinny_kernel<W_BIT, XDT, GS, MT, NT, DEPTH, WAVES>,
                        dim3((unsigned)blocks), dim3(64 * WAVES), a.stream, a.x, a.Q, a.scales,
                        a.zeros, a.y, a.M, a.N, a.K,

@@ -246,8 +246,12 @@ static qmm_status gemm_impl(const char* fn, const void* x, const void* Q, const 
   if (!gemm_shape_ok(N, K, w_bit))
     return fail(QMM_ERR_UNSUPPORTED, "%s: tile layout needs N %% 16 == 0 and K %% %d == 0", fn,
                 qmm::mfma_kblock(w_bit));
+  // the kernels carry their column-tile count in 24 bits (N / 16 < 2^24)
+  if (N >= (1 << 28))
+    return fail(QMM_ERR_UNSUPPORTED, "%s: N=%d too large (N < 2^28)", fn, N);
   const int gs = gemm_group(K, group_size);
-  const qmm::GemmPlan p = qmm::plan_gemm(M, N, K, w_bit, gs);
+  // without a workspace the plan keeps every partial sum inside a workgroup
+  const qmm::GemmPlan p = qmm::plan_gemm(M, N, K, w_bit, gs, workspace != nullptr);
   if (p.kind < 0) return fail(QMM_ERR_UNSUPPORTED, "%s: no MFMA kernel for this shape", fn);
   // the skinny kernel addresses a workgroup's x rows (up to 64 rows of K)
   // and weight strips with 32-bit byte offsets

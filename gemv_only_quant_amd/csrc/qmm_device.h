@@ -23,18 +23,21 @@ template <class F>
 __device__ __forceinline__ void with_y(void* y, int ydt, F&& f);
 
 // Options carried in the top bits of a kernel's tile-count argument, so no
-// kernel needs more than 56 bytes of explicit arguments: on this runtime one
-// argument more (a 320-byte instead of a 312-byte argument segment, with the
-// hidden arguments) measured +0.3 us on every launch of a 6 us kernel.
-//   bits 0-27 tile count, bits 28-29 output type, bit 30 per-column scales
-constexpr int kTileBits = 28;
-__host__ __device__ constexpr int pack_tiles(int tiles, int ydt, bool per_column) {
-  return tiles | (ydt << kTileBits) | ((per_column ? 1 : 0) << (kTileBits + 2));
+// kernel needs more than 56 bytes of explicit arguments (64 with a
+// workspace): on this runtime one argument more (a 320-byte instead of a
+// 312-byte argument segment, with the hidden arguments) measured +0.3 us on
+// every launch of a 6 us kernel.
+//   bits 0-23 tile count, bits 24-27 K splits - 1, bits 28-29 output type,
+//   bit 30 per-column scales
+constexpr int kTileBits = 24;
+__host__ __device__ constexpr int pack_tiles(int tiles, int ydt, bool per_column, int splits = 1) {
+  return tiles | ((splits - 1) << kTileBits) | (ydt << 28) | ((per_column ? 1 : 0) << 30);
 }
 __device__ __forceinline__ int tiles_of(int t) { return t & ((1 << kTileBits) - 1); }
-__device__ __forceinline__ int ydt_of(int t) { return (t >> kTileBits) & 3; }
+__device__ __forceinline__ int splits_of(int t) { return ((t >> kTileBits) & 15) + 1; }
+__device__ __forceinline__ int ydt_of(int t) { return (t >> 28) & 3; }
 // group-index mask: 0 (every group is group 0) for per-column scales
-__device__ __forceinline__ int gmask_of(int t) { return ((t >> (kTileBits + 2)) & 1) ? 0 : -1; }
+__device__ __forceinline__ int gmask_of(int t) { return ((t >> 30) & 1) ? 0 : -1; }
 
 template <class F>
 __device__ __forceinline__ void with_y(void* y, int ydt, F&& f) {
@@ -121,6 +124,19 @@ __device__ __forceinline__ uint32_t buf_load32(buf_t b, int off) {
 }
 __device__ __forceinline__ uint32_t buf_load16(buf_t b, int off) {
   return __builtin_amdgcn_raw_buffer_load_b16(b, off, 0, 0);
+}
+
+// Accesses coherent across the XCDs' L2 caches without a fence: the sc1
+// cache-policy bit (the one the compiler gives agent-scope atomic loads and
+// stores on gfx950) makes a store write through this XCD's L2 and a load
+// fetch past any copy an L2 may hold.  An agent-scope fence would instead
+// write back and invalidate the whole L2 of the XCD.
+constexpr int kCoherent = 16;  // sc1
+__device__ __forceinline__ void buf_store128_coherent(u32x4_t v, buf_t b, int off) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, b, off, 0, kCoherent);
+}
+__device__ __forceinline__ u32x4_t buf_load128_coherent(buf_t b, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(b, off, 0, kCoherent);
 }
 
 __device__ __forceinline__ int xcd_remap(int b, int total) {

@@ -74,11 +74,14 @@ struct GemmPlan {
   int mtile;     // rows per M tile
   int nt;        // 16-column strips per workgroup (skinny)
   int waves;     // waves per workgroup, splitting K (skinny: 4 or 8)
+  int splits;    // workgroups per tile splitting K (skinny; 1 = none)
   int n_tiles;
   int m_tiles;
-  size_t workspace_bytes;  // always 0 in this version: no kernel needs one
+  size_t workspace_bytes;  // tickets + partial tiles when splits > 1, else 0
 };
-GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size);
+// with_workspace: whether the call has a workspace; without one the plan
+// never splits K over workgroups.
+GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size, bool with_workspace = true);
 hipError_t launch_gemm(const MatmulArgs& a, const GemmPlan& p);
 
 // ---- int8 x ternary (ternary.hip) -----------------------------------------

@@ -123,14 +123,24 @@ QMM_API qmm_status qmm_unpack_layout(const void* Q_mfma, void* Q_canon, int N, i
                              void* stream);
 
 /*
- * Scratch device memory that qmm_gemv / qmm_gemm need for the given shape
- * beyond their inputs and outputs (cf. the lock workspace Marlin's
- * marlin_cuda() takes from its caller).  The kernels of this version keep
- * every partial sum inside a workgroup, so the size is 0 for every shape
- * and the workspace argument may be NULL; a nonzero size, if a later
- * scheduler needs one, is caller-owned memory of at least that many bytes,
- * 16-byte aligned, and calls that may run concurrently would need distinct
- * workspaces.  Returns 0 for invalid arguments too.
+ * Scratch device memory a qmm_gemm / qmm_gemm_ex call can use for the given
+ * shape beyond its inputs and outputs (cf. the lock workspace Marlin's
+ * marlin_cuda() takes from its caller, and its striped partition of K over
+ * thread blocks with a global reduction).  Nonzero for shapes whose column
+ * tiles alone leave most compute units idle: K is then split over several
+ * workgroups per tile, which leave partial tiles and an arrival ticket per
+ * tile in the workspace; the last workgroup of a tile to arrive adds the
+ * partials in a fixed order and writes y.
+ *   - Caller-owned device memory of at least this many bytes, 16-byte
+ *     aligned, ZERO-FILLED before its first use.  Every call leaves it
+ *     re-armed (all tickets back at zero), so one workspace serves any
+ *     sequence of calls on one stream; calls that may run concurrently need
+ *     distinct workspaces.
+ *   - A NULL workspace is always accepted: the call then runs a plan that
+ *     keeps every partial sum inside a workgroup (slower on such shapes).
+ *     A non-NULL one smaller than this size is QMM_ERR_ARG.
+ *   - qmm_gemv and the ternary product never use one.
+ * Returns 0 for shapes that need none and for invalid arguments.
  */
 QMM_API size_t qmm_workspace_bytes(int M, int N, int K, int w_bit, int group_size);
 

@@ -41,10 +41,16 @@ def test_version_and_sizes():
     assert qmm.qmm_workspace_bytes(1, 64, 100, 4, 128) == 0  # invalid: K % group
     assert qmm.qmm_workspace_bytes(16, 4096, 4096, 4, qmm.QMM_PER_COLUMN) == 0
     assert qmm.qmm_workspace_bytes(1, 64, 40, 4, qmm.QMM_PER_COLUMN) == 0  # K % 32
-    # no built kernel needs a workspace: nothing leaves a workgroup but y
-    for M, N, K, wb, g in [(1, 4096, 4096, 4, 128), (16, 14336, 4096, 8, 0),
-                           (16, 8192, 8192, 4, 128), (4096, 11008, 4096, 2, 64)]:
+    # grids with enough column tiles, and the prefill kernel, keep every
+    # partial sum inside a workgroup: no workspace
+    for M, N, K, wb, g in [(16, 8192, 8192, 4, 128), (4096, 11008, 4096, 2, 64),
+                           (4096, 64, 4096, 4, 128)]:
         assert qmm.qmm_workspace_bytes(M, N, K, wb, g) == 0
+    # few column tiles over a long K: K split over workgroups, tickets + partials
+    M, N, K = 16, 1024, 14336
+    need = qmm.qmm_workspace_bytes(M, N, K, 4, 128)
+    tiles = N // 16
+    assert need > tiles * 16 * 16 * 4 and need % 16 == 0
 
 
 def call_gemv(**kw):

@@ -13,12 +13,20 @@ qmm = pytest.importorskip("gemv_only_quant_amd")
 pytestmark = pytest.mark.gpu
 
 
+NO_WORKSPACE = "none"
+
+
 def run_gemm(case, ws=None):
+    """qmm_gemm on the case; ws None: the cached workspace the shape calls
+    for; NO_WORKSPACE: a NULL workspace (the plan that splits nothing over
+    workgroups); else the given tensor."""
     d = case.to("cuda")
     Qt = qmm.pack(d.Q, case.N, case.K, case.w_bit)
     y = torch.full((case.M, case.N), float("nan"), dtype=torch.float32, device="cuda")
     if ws is None:
         ws = qmm.workspace_for(case.M, case.N, case.K, case.w_bit, case.group_size, "cuda")
+    elif isinstance(ws, str):
+        ws = None
     qmm.qmm_gemm(d.x, Qt, d.scales, d.zeros, y, case.M, case.N, case.K, case.w_bit,
                  case.group_size, workspace=ws)
     return cpu(y)
@@ -185,40 +193,82 @@ def test_gemm_large_one_hot_reproduces_weights():
         assert np.array_equal(y[m], W[k]), (m, k)
 
 
-# ------------------------------------ small N, long K: 8 waves split K per tile
-# Shapes whose tiles alone leave most CUs idle (< 128 tiles, >= 16 stages of
-# K): the planner gives each workgroup 8 waves that split K.
+# ------------------------------------ small N, long K: K split over workgroups
+# Shapes whose tiles alone leave most CUs idle.  With a workspace, K is split
+# over several workgroups per tile and the last to arrive adds the partials;
+# with a NULL workspace the planner gives each workgroup 8 waves instead
+# (>= 16 stages of K), so both plans are checked on the same shapes.
 MANYWAVES = [  # M, N, K, w_bit, group, x_dtype, symmetric
     (16, 64, 4096, 4, 128, si.F16, False),      # 4 tiles, 32 stages
     (3, 256, 8192, 4, 64, si.BF16, False),      # ragged M
     (1, 32, 6144, 4, 256, si.F16, True),        # 48 stages: uneven shares
-    (16, 80, 5120, 4, 32, si.BF16, False),      # 40 stages over 8 waves, g32
+    (16, 80, 5120, 4, 32, si.BF16, False),      # 40 stages, g32
     (30, 48, 4096, 4, 128, si.F16, False),      # two 16-row tiles
     (16, 48, 8192, 2, 64, si.BF16, False),      # int2
-    (9, 16, 2176, 4, 128, si.BF16, False),      # 17 stages: 3 per wave, waves 6 and 7 idle
+    (9, 16, 2176, 4, 128, si.BF16, False),      # 17 stages: uneven splits, idle waves
+    (64, 112, 4096, 4, 128, si.BF16, False),    # 64-row tile, 7 strips
 ]
 
 
+@pytest.mark.parametrize("plan", ["split", "waves"])
 @pytest.mark.parametrize("M,N,K,w_bit,gs,xdt,sym", MANYWAVES)
-def test_gemm_many_waves_within_bound(M, N, K, w_bit, gs, xdt, sym):
+def test_gemm_small_grid_within_bound(M, N, K, w_bit, gs, xdt, sym, plan):
     case = si.lowbit_case(M, N, K, w_bit, gs, xdt, sym, seed=900 + M + N + K)
-    y = run_gemm(case)
+    if plan == "split":
+        assert qmm.qmm_workspace_bytes(M, N, K, w_bit, gs) > 0
+    y = run_gemm(case, ws=None if plan == "split" else NO_WORKSPACE)
     y_ref, a_ref = oracle.qmm(*case.oracle_args())
-    assert_within_bound(y, y_ref, a_ref, f"waves w{w_bit} M{M} N{N} K{K}")
+    assert_within_bound(y, y_ref, a_ref, f"{plan} w{w_bit} M{M} N{N} K{K}")
 
 
-@pytest.mark.parametrize("M,N,K,xdt", [(16, 64, 8192, si.BF16), (7, 32, 4096, si.F16)])
-def test_gemm_many_waves_int8_within_bound(M, N, K, xdt):
+@pytest.mark.parametrize("plan", ["split", "waves"])
+@pytest.mark.parametrize("M,N,K,xdt", [(16, 64, 8192, si.BF16), (7, 32, 4096, si.F16),
+                                        (40, 48, 4096, si.BF16)])
+def test_gemm_small_grid_int8_within_bound(M, N, K, xdt, plan):
     case = si.int8_case(M, N, K, xdt, seed=950 + M + K)
-    y = run_gemm(case)
+    y = run_gemm(case, ws=None if plan == "split" else NO_WORKSPACE)
     y_ref, a_ref = oracle.qmm(*case.oracle_args())
-    assert_within_bound(y, y_ref, a_ref, f"waves int8 M{M} N{N} K{K}")
+    assert_within_bound(y, y_ref, a_ref, f"{plan} int8 M{M} N{N} K{K}")
 
 
+@pytest.mark.parametrize("plan", ["split", "waves"])
 @pytest.mark.parametrize("M,N,K,w_bit,gs", [(16, 64, 4096, 4, 128), (5, 32, 8192, 2, 64),
-                                             (20, 16, 4096, 4, 64)])
-def test_gemm_many_waves_exact_probe_bit_exact(M, N, K, w_bit, gs):
+                                             (20, 16, 4096, 4, 64), (33, 32, 2048, 4, 32)])
+def test_gemm_small_grid_exact_probe_bit_exact(M, N, K, w_bit, gs, plan):
     case = si.exact_lowbit_case(M, N, K, w_bit, gs, si.BF16, False, seed=M + N)
-    y = run_gemm(case)
+    y = run_gemm(case, ws=None if plan == "split" else NO_WORKSPACE)
     y_ref, _ = oracle.qmm(*case.oracle_args())
     assert np.array_equal(y.astype(np.float64), y_ref)
+
+
+def test_split_workspace_rearmed_over_calls():
+    """One zero-filled workspace through calls of different shapes (different
+    tile and split counts): each result is right, and after every call the
+    tickets are back at zero."""
+    ws = torch.zeros(16 << 20, dtype=torch.uint8, device="cuda")
+    shapes = [(16, 64, 4096, 4, 128), (16, 1024, 14336, 4, 128), (3, 32, 8192, 2, 64),
+              (16, 64, 4096, 4, 128), (40, 48, 4096, 8, 0), (1, 16, 2048, 4, 128)]
+    for i, (M, N, K, wb, gs) in enumerate(shapes):
+        need = qmm.qmm_workspace_bytes(M, N, K, wb, gs)
+        assert 0 < need <= ws.numel(), (M, N, K, need)
+        case = (si.int8_case(M, N, K, si.BF16, seed=70 + i) if wb == 8 else
+                si.exact_lowbit_case(M, N, K, wb, gs, si.F16, False, seed=70 + i))
+        for rep in range(3):
+            y = run_gemm(case, ws=ws)
+            y_ref, a_ref = oracle.qmm(*case.oracle_args())
+            if wb == 8:
+                assert_within_bound(y, y_ref, a_ref, f"call {i}.{rep}")
+            else:
+                assert np.array_equal(y.astype(np.float64), y_ref), f"call {i}.{rep}"
+            # every shape here has <= 64 tiles: its tickets are the first 256 bytes
+            assert int(torch.count_nonzero(ws[:256])) == 0, f"tickets left armed after {i}"
+
+
+def test_split_undersized_workspace_refused():
+    M, N, K = 16, 64, 4096
+    need = qmm.qmm_workspace_bytes(M, N, K, 4, 128)
+    assert need > 0
+    case = si.lowbit_case(M, N, K, 4, 128, si.F16, False, seed=5)
+    with pytest.raises(qmm.QmmError) as e:
+        run_gemm(case, ws=torch.zeros(need - 16, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == qmm.QMM_ERR_ARG
