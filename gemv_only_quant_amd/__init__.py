@@ -20,6 +20,7 @@ QMM_OK, QMM_ERR_ARG, QMM_ERR_UNSUPPORTED, QMM_ERR_DEVICE = 0, 1, 2, 3
 QMM_F16, QMM_BF16, QMM_F32 = 0, 1, 2
 QMM_PER_COLUMN = -1  # group_size for per-column scales (one group spanning K)
 QMM_LAYOUT_CANON, QMM_LAYOUT_MFMA = 0, 1
+QMM_NOALLOC_SCRATCH_BYTES = 8 << 20  # scratch held per GPU for qmm_gemm_noalloc
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run python gemv_only_quant_amd/build.py")
@@ -40,19 +41,20 @@ _lib.qmm_gemv.argtypes = _MATMUL
 _lib.qmm_gemm.argtypes = _MATMUL
 _lib.qmm_gemv_ex.argtypes = _MATMUL_EX
 _lib.qmm_gemm_ex.argtypes = _MATMUL_EX
+_lib.qmm_gemm_noalloc.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P]
 _lib.qmm_dequant.argtypes = [_P, _I, _P, _P, _P, _I, _I, _I, _I, _P]
 _lib.qmm_t2_pack.argtypes = [_P, _P, _I, _I, _P]
 _lib.qmm_t2_unpack_layout.argtypes = [_P, _P, _I, _I, _P]
 _lib.qmm_i8t2_gemm.argtypes = [_P, _P, _P, _I, _I, _I, _P]
 _lib.qmm_quantize.argtypes = [_P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _P]
 for _f in ("qmm_pack", "qmm_unpack_layout", "qmm_gemv", "qmm_gemm", "qmm_gemv_ex", "qmm_gemm_ex",
-           "qmm_dequant", "qmm_t2_pack", "qmm_t2_unpack_layout", "qmm_i8t2_gemm", "qmm_quantize"):
+           "qmm_gemm_noalloc", "qmm_dequant", "qmm_t2_pack", "qmm_t2_unpack_layout", "qmm_i8t2_gemm", "qmm_quantize"):
     getattr(_lib, _f).restype = _I
 
 EXPORTS = ("qmm_version", "qmm_last_error", "qmm_packed_bytes", "qmm_pack",
            "qmm_unpack_layout", "qmm_workspace_bytes", "qmm_gemv", "qmm_gemm", "qmm_gemv_ex",
-           "qmm_gemm_ex", "qmm_dequant", "qmm_t2_pack", "qmm_t2_unpack_layout", "qmm_i8t2_gemm",
-           "qmm_quantize")
+           "qmm_gemm_ex", "qmm_gemm_noalloc", "qmm_dequant", "qmm_t2_pack", "qmm_t2_unpack_layout",
+           "qmm_i8t2_gemm", "qmm_quantize")
 
 
 class QmmError(ValueError):
@@ -267,6 +269,24 @@ def qmm_gemm_ex(x, Q, scales, zeros, y, M, N, K, w_bit, group_size, y_dtype=None
                 workspace=None, workspace_bytes=None, stream=None):
     _matmul_ex(_lib.qmm_gemm_ex, "qmm_gemm_ex", x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit,
                group_size, x_dtype, workspace, workspace_bytes, stream)
+
+
+def qmm_gemm_noalloc(x, Q, scales, zeros, y, M, N, K, w_bit, group_size, y_dtype=None,
+                     x_dtype=None, stream=None):
+    """qmm_gemm_ex with no workspace and no allocation: the library's own
+    per-GPU scratch holds what a split of K needs (calls overlapping on one
+    GPU race; the stream must be on the current device)."""
+    if x_dtype is None:
+        x_dtype = _dtype_code(x)
+    if y_dtype is None:
+        y_dtype = _y_code(y)
+    y_dtypes = ({QMM_F32: (torch.float32,), QMM_F16: (torch.float16,),
+                 QMM_BF16: (torch.bfloat16,)}.get(y_dtype, _YS))
+    a, (px, pq, ps, pz, py, _) = _matmul_ptrs("qmm_gemm_noalloc", x, Q, scales, zeros, y,
+                                              _Y_SIZE.get(y_dtype, 0), y_dtypes, M, N, K, w_bit,
+                                              group_size, None, 0)
+    _check(_lib.qmm_gemm_noalloc(px, pq, ps, pz, py, y_dtype, M, N, K, w_bit, group_size,
+                                 x_dtype, a.stream(stream)))
 
 
 def qmm_dequant(Q, layout, scales, zeros, w_out, N, K, w_bit, group_size, stream=None):

@@ -7,8 +7,18 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "../../include/qmm.h"
 #include "qmm_internal.h"
+
+// ---- scratch of the allocation-free entry point (qmm_gemm_noalloc) --------
+// One copy of this array exists on every GPU the library runs on, for the
+// life of the process.  In host code its name is only a stand-in for the
+// device address: that address is taken once per device with
+// hipGetSymbolAddress (scratch_of_current_device) and only it is passed to
+// kernels.
+static __device__ __align__(256) unsigned char scratch[QMM_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -125,6 +135,35 @@ int gemm_group(int K, int group_size) {
 }
 int group_mask(int group_size) { return group_size == QMM_PER_COLUMN ? 0 : -1; }
 
+// Zeroes the tickets at the head of the scratch before a call that uses it
+// (a kernel, not a memset, so the call can be captured in a HIP graph).
+__global__ void clear_tickets_kernel(uint32_t* t, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) t[i] = 0u;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array, looked up on the
+// first call on that device (with it current) and kept.
+hipError_t scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 namespace qmm {
@@ -234,10 +273,12 @@ static qmm_status gemv_impl(const char* fn, const void* x, const void* Q, const 
   return device_status(fn, qmm::launch_gemv_lowbit(a, p));
 }
 
+// noalloc: the allocation-free entry point -- the workspace is the current
+// device's scratch array, its tickets cleared first on `stream`.
 static qmm_status gemm_impl(const char* fn, const void* x, const void* Q, const void* scales,
                             const void* zeros, void* y, int y_dtype, int M, int N, int K,
                             int w_bit, int group_size, int x_dtype, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            size_t workspace_bytes, void* stream, bool noalloc = false) {
   bool noop = false;
   qmm_status st = check_matmul(fn, x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit, group_size,
                                x_dtype, &noop);
@@ -251,7 +292,7 @@ static qmm_status gemm_impl(const char* fn, const void* x, const void* Q, const 
     return fail(QMM_ERR_UNSUPPORTED, "%s: N=%d too large (N < 2^28)", fn, N);
   const int gs = gemm_group(K, group_size);
   // without a workspace the plan keeps every partial sum inside a workgroup
-  const qmm::GemmPlan p = qmm::plan_gemm(M, N, K, w_bit, gs, workspace != nullptr);
+  const qmm::GemmPlan p = qmm::plan_gemm(M, N, K, w_bit, gs, noalloc || workspace != nullptr);
   if (p.kind < 0) return fail(QMM_ERR_UNSUPPORTED, "%s: no MFMA kernel for this shape", fn);
   // the skinny kernel addresses a workgroup's x rows (up to 64 rows of K)
   // and weight strips with 32-bit byte offsets
@@ -264,10 +305,39 @@ static qmm_status gemm_impl(const char* fn, const void* x, const void* Q, const 
       return fail(QMM_ERR_UNSUPPORTED, "%s: scale table of %lld x %d too large (< 2^30 entries)",
                   fn, (long long)G, N);
   }
-  st = check_workspace(fn, p.workspace_bytes, workspace, workspace_bytes);
-  if (st != QMM_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (noalloc) {
+    if (p.workspace_bytes > QMM_NOALLOC_SCRATCH_BYTES)
+      return fail(QMM_ERR_UNSUPPORTED,
+                  "%s: this shape needs %zu bytes of scratch, more than the %zu the "
+                  "allocation-free entry point holds (use qmm_gemm_ex with a workspace)",
+                  fn, p.workspace_bytes, (size_t)QMM_NOALLOC_SCRATCH_BYTES);
+    workspace = nullptr;
+    if (p.workspace_bytes > 0) {
+      int cur = 0;
+      hipError_t e = hipGetDevice(&cur);
+      if (e != hipSuccess) return device_status(fn, e);
+      if (s != nullptr) {
+        hipDevice_t sd = 0;
+        e = hipStreamGetDevice(s, &sd);
+        if (e != hipSuccess) return device_status(fn, e);
+        if ((int)sd != cur)
+          return fail(QMM_ERR_ARG, "%s: stream belongs to device %d, the current device is %d",
+                      fn, (int)sd, cur);
+      }
+      e = scratch_of_current_device(&workspace);
+      if (e != hipSuccess) return device_status(fn, e);
+      const int tickets = (int)(((long)p.n_tiles * p.m_tiles + 63) & ~63L);
+      e = qmm::launch_kernel(clear_tickets_kernel, dim3((tickets + 255) / 256), dim3(256), s,
+                             workspace, tickets);
+      if (e != hipSuccess) return device_status(fn, e);
+    }
+  } else {
+    st = check_workspace(fn, p.workspace_bytes, workspace, workspace_bytes);
+    if (st != QMM_OK) return st;
+  }
   qmm::MatmulArgs a{x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit, gs, group_mask(group_size),
-                    x_dtype, workspace, reinterpret_cast<hipStream_t>(stream)};
+                    x_dtype, workspace, s};
   return device_status(fn, qmm::launch_gemm(a, p));
 }
 
@@ -297,6 +367,13 @@ qmm_status qmm_gemm_ex(const void* x, const void* Q, const void* scales, const v
                        int x_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   return gemm_impl("qmm_gemm_ex", x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit, group_size,
                    x_dtype, workspace, workspace_bytes, stream);
+}
+
+qmm_status qmm_gemm_noalloc(const void* x, const void* Q, const void* scales, const void* zeros,
+                            void* y, int y_dtype, int M, int N, int K, int w_bit, int group_size,
+                            int x_dtype, void* stream) {
+  return gemm_impl("qmm_gemm_noalloc", x, Q, scales, zeros, y, y_dtype, M, N, K, w_bit,
+                   group_size, x_dtype, nullptr, 0, stream, true);
 }
 
 qmm_status qmm_dequant(const void* Q, int layout, const void* scales, const void* zeros,

@@ -186,6 +186,26 @@ QMM_API qmm_status qmm_gemm_ex(const void* x, const void* Q, const void* scales,
                                size_t workspace_bytes, void* stream);
 
 /*
+ * qmm_gemm_noalloc: qmm_gemm_ex for callers that cannot allocate device
+ * memory -- code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It allocates nothing and takes no workspace:
+ * where the plan splits K over workgroups (see qmm_workspace_bytes), the
+ * tickets and partial tiles live in a scratch array the library holds on
+ * each GPU it runs on (QMM_NOALLOC_SCRATCH_BYTES, kept until the process
+ * ends), and a small kernel clears the tickets on `stream` before the
+ * product.  Every call on a GPU shares that GPU's array, so calls that may
+ * overlap on one GPU (on different streams) race: the caller serialises
+ * them.  `stream` must belong to the current device (else QMM_ERR_ARG).  A
+ * shape whose plan needs more scratch than the array holds is
+ * QMM_ERR_UNSUPPORTED (qmm_gemm_ex with a workspace takes any size).
+ * Operands, results and all other errors as qmm_gemm_ex.
+ */
+#define QMM_NOALLOC_SCRATCH_BYTES (8u << 20)
+QMM_API qmm_status qmm_gemm_noalloc(const void* x, const void* Q, const void* scales,
+                                    const void* zeros, void* y, int y_dtype, int M, int N,
+                                    int K, int w_bit, int group_size, int x_dtype, void* stream);
+
+/*
  * qmm_dequant: W (K, N) fp32 from Q in either layout, bit-exact:
  * W[k][n] = float(q - z) * float(s) for low-bit (exact in fp32), and
  * W[k][n] = float(Q[n][k]) for int8 (row scale NOT applied).  For tests.
