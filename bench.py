@@ -469,8 +469,15 @@ def trace_summary(db_path):
     Prints a Markdown table: dispatches, mean, median, p90, min, max (µs)."""
     import sqlite3
     c = sqlite3.connect(db_path)
-    regions = c.execute("select name, start, end from regions where name like 'timed %' "
-                        "order by start").fetchall()
+    regions = []
+    for name, extdata, r0, r1 in c.execute("select name, extdata, start, end from regions "
+                                           "order by start"):
+        try:  # the range's message is the name, or (rocprofv3) extdata's "message"
+            msg = json.loads(extdata or "{}").get("message", name)
+        except ValueError:
+            msg = name
+        if msg and msg.startswith("timed "):
+            regions.append((msg, r0, r1))
     kern = c.execute("select name, start, end from kernels order by start").fetchall()
     by = {}
     j = 0
