@@ -1,14 +1,16 @@
 """Benchmark of the weight-only quantized matmul on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
-    python bench.py --probe WORKLOAD      (three calls, for rocprofv3 --pmc)
+    python bench.py --probe WORKLOAD[@ENTRY]  (three calls, for rocprofv3 --pmc)
     python bench.py --trace-summary DB    (per-workload rows of a rocprofv3 trace
                                            taken with --kernel-trace --marker-trace)
 
 A step is one call of the hot path on one batch of synthetic input already
 resident in HBM.  The headline workload is the int4 group-128 asymmetric
-decode GEMV (M=1, K=N=4096, fp16 x, fp32 accumulation); `value` is its
+decode GEMV (M=1, K=N=4096, fp16 x, fp32 accumulation), through qmm_gemm on
+weights repacked once by qmm_pack (offline, not timed); `value` is its
 effective weight bandwidth (packed weights + scales + zeros per call / time).
+The same product through qmm_gemv on the canonical layout is a workload line.
 Every other workload is timed the same way and reported under "workloads";
 the prefill GEMM (M=4096) is reported in TFLOP/s under "prefill".
 
@@ -45,7 +47,9 @@ INT8_PEAK_TOPS = 5000.0         # MI355X dense int8 matrix peak
 POOL_BYTES = 512 << 20          # weight pool for memory-bound workloads
 
 HEADLINE = "int4_g128_asym_gemv_m1_k4096_n4096"
+HEADLINE_PATH = "gemm"  # qmm_gemm on the tile layout (qmm_pack, offline): the decode GEMV
 OTHERS = [  # (workload, entry)
+    (HEADLINE, "gemv"),  # the same product on the canonical layout (qmm_gemv)
     ("int8_gemv_m1_k1024_n1024", "gemv"),
     ("int4_pc_sym_gemv_m1_k4096_n4096", "gemv"),  # per-column scales
     ("int8_skinny_m16_k4096_n14336", "gemm"),
@@ -315,16 +319,17 @@ def time_quantize(K, N, w_bit, group_size, steps=20):
             "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
 
 
-def traffic_for(name):
-    """HBM bytes per launch from the committed counter summary, if the kernel
-    source it was taken with is unchanged; else None."""
+def traffic_for(name, path):
+    """HBM bytes per launch of workload `name` through qmm_<path> from the
+    committed counter summary, if the kernel source it was taken with is
+    unchanged; else None."""
     try:
         text = open(TRAFFIC_FILE).read()
     except OSError:
         return None
     for m in re.finditer(r"^traffic_bytes_per_launch:\s+(\S+)\s+(\d+)\s+(\S+)\s+([0-9a-f]+)\s*$",
                          text, re.M):
-        if m.group(1) != name:
+        if m.group(1) != f"{name}@qmm_{path}":
             continue
         src = os.path.join(CSRC, m.group(3))
         try:
@@ -423,13 +428,13 @@ def line(r, path):
            "hbm_frac": round(r["tbytes"] / us / 1e3 / HBM_PEAK_GBS, 4),
            "tflops": round(r["flops"] / us / 1e6, 2),
            "mfma_frac": round(r["flops"] / us / 1e6 / MFMA_PEAK_TFLOPS, 4)}
-    t = traffic_for(case.name)
+    t = traffic_for(case.name, path)
     if t is not None:
         out["traffic_bytes"] = t
     return out
 
 
-def probe(name):
+def probe(spec):
     """Counter probe for rocprofv3 --pmc: three calls of one workload's entry
     point, each on its own copy of the weights (a pool of >= 512 MB, so no
     call finds its weights in cache), then three copies of a 256 MiB device
@@ -439,20 +444,37 @@ def probe(name):
     import gemv_only_quant_amd as qmm
     import synth_inputs as si
 
-    path = "gemv" if name == HEADLINE or dict(OTHERS).get(name) == "gemv" else "gemm"
-    case = si.workload(name)
-    wbytes, _ = bytes_of(case)
-    d = case.to("cuda")
-    Q0 = d.Q if path == "gemv" else qmm.pack(d.Q, case.N, case.K, case.w_bit)
-    copies = max(3, -(-POOL_BYTES // wbytes))
-    pool = [(Q0.clone(), d.scales.clone(), None if d.zeros is None else d.zeros.clone())
-            for _ in range(copies)]
-    y = torch.empty((case.M, case.N), dtype=torch.float32, device="cuda")
-    fn = qmm.qmm_gemv if path == "gemv" else qmm.qmm_gemm
-    torch.cuda.synchronize()
-    for i in range(3):
-        Q, s, z = pool[(i * copies) // 3]
-        fn(d.x, Q, s, z, y, case.M, case.N, case.K, case.w_bit, case.group_size)
+    name, _, entry = spec.partition("@")  # WORKLOAD[@qmm_gemv|@qmm_gemm]
+    if name in TERNARY:
+        case = si.workload(name)
+        d = case.to("cuda")
+        Wt = qmm.t2_pack(d.Wp, case.N, case.K)
+        copies = max(3, -(-POOL_BYTES // Wt.numel())) if case.M < 1024 else 3
+        pool = [Wt.clone() for _ in range(copies)]
+        y = torch.empty((case.M, case.N), dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        for i in range(3):
+            qmm.qmm_i8t2_gemm(d.A, pool[(i * copies) // 3], y, case.M, case.N, case.K)
+        path = "i8t2_gemm"
+    else:
+        if entry:
+            path = entry.replace("qmm_", "")
+        else:
+            path = HEADLINE_PATH if name == HEADLINE else dict(OTHERS).get(name, "gemm")
+        case = si.workload(name)
+        wbytes, _ = bytes_of(case)
+        d = case.to("cuda")
+        Q0 = d.Q if path == "gemv" else qmm.pack(d.Q, case.N, case.K, case.w_bit)
+        copies = max(3, -(-POOL_BYTES // wbytes)) if case.M < 1024 else 3
+        pool = [(Q0.clone(), d.scales.clone(), None if d.zeros is None else d.zeros.clone())
+                for _ in range(copies)]
+        y = torch.empty((case.M, case.N), dtype=torch.float32, device="cuda")
+        ws = qmm.workspace_for(case.M, case.N, case.K, case.w_bit, case.group_size, "cuda")
+        fn = qmm.qmm_gemv if path == "gemv" else qmm.qmm_gemm
+        torch.cuda.synchronize()
+        for i in range(3):
+            Q, s, z = pool[(i * copies) // 3]
+            fn(d.x, Q, s, z, y, case.M, case.N, case.K, case.w_bit, case.group_size, workspace=ws)
     torch.cuda.synchronize()
     src = torch.ones(1 << 27, dtype=torch.int16, device="cuda")  # 256 MiB
     dst = torch.empty_like(src)
@@ -526,7 +548,7 @@ def main():
     if args.probe:
         probe(args.probe)
         return
-    r = time_workload(HEADLINE, args.steps, args.warmup, "gemv")
+    r = time_workload(HEADLINE, args.steps, args.warmup, HEADLINE_PATH)
     case, us = r["case"], r["us"]
     achieved = r["tbytes"] / (us * 1e-6) / 1e9
     out = {
@@ -544,14 +566,17 @@ def main():
         "data": "synthetic",
         "config": {"workload": HEADLINE, "M": case.M, "N": case.N, "K": case.K,
                    "w_bit": case.w_bit, "group_size": case.group_size,
-                   "zeros": case.zeros is not None, "accumulate": "f32", "entry": "qmm_gemv",
+                   "zeros": case.zeros is not None, "accumulate": "f32",
+                   "entry": f"qmm_{HEADLINE_PATH}",
+                   "layout": "tile layout written once by qmm_pack from the canonical qw "
+                             "(offline, not timed)" if HEADLINE_PATH == "gemm" else "canonical",
                    "weight_pool_copies": r["copies"], "weight_copies_rotated": r["rotated"],
                    "rotated_MB": round(r["rotated_bytes"] / 1e6, 1),
                    "timing": "hip graph replay, 1 GiB cache eviction before each timed replay",
                    "eager_us_per_call": round(r["eager_us"], 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_for(HEADLINE)},
+                     "traffic": traffic_for(HEADLINE, HEADLINE_PATH)},
     }
     if not args.quick:
         out["workloads"] = [line(time_workload(n, 200, 20, p), p) for n, p in OTHERS]
@@ -565,7 +590,7 @@ def main():
                         "y_dtype": out_dt, "us_per_call": round(p["us"], 2),
                         "tflops": round(tf, 2), "peak_tflops": MFMA_PEAK_TFLOPS,
                         "frac": round(tf / MFMA_PEAK_TFLOPS, 4)})
-            t = traffic_for(n) if out_dt == "f32" else None
+            t = traffic_for(n, "gemm") if out_dt == "f32" else None
             if t is not None:
                 pre[-1]["traffic_bytes"] = t
         out["prefill"] = pre

@@ -869,6 +869,24 @@ GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size, bool with_wor
     p.workspace_bytes = 0;
     return p;
   }
+  // Low-bit decode: the VALU GEMV on the tile layout, one strip per
+  // workgroup, every wave load 1 KiB of consecutive bytes.  Measured at
+  // K=N=4096 (us; this GEMV / the skinny MFMA kernel below): int4 g128 M=1
+  // 4.81 / 6.23, M=2 5.38 / 6.25, M=4 6.50 / 6.30; int2 g64 M=1 5.29 / 7.55,
+  // M=4 7.08 / 7.57; int4 g32 M=4 8.65 / 7.93.  So M <= 2, and int2 to M=4.
+  static const int want_tile = env_int("QMM_GEMV_TILE");
+  const bool tile = M <= 2 || (w_bit == 2 && M <= kGemvTileMaxM);
+  if (w_bit != 8 && (want_tile > 0 ? M <= kGemvTileMaxM : tile) && want_tile != 0) {
+    p.kind = 2;
+    p.mtile = M;
+    p.n_tiles = N / 16;
+    p.m_tiles = 1;
+    p.nt = 1;
+    p.waves = 4;
+    p.splits = 1;
+    p.workspace_bytes = 0;
+    return p;
+  }
   int mt, nt;
   skinny_shape(M, N, &mt, &nt);
   p.kind = 0;
@@ -1005,6 +1023,7 @@ static hipError_t launch_large(const MatmulArgs& a, const GemmPlan& p) {
 
 hipError_t launch_gemm(const MatmulArgs& a, const GemmPlan& p) {
   const bool f16 = a.x_dtype == XF16;
+  if (p.kind == 2) return launch_gemv_tile(a);
   if (p.kind == 1) {
     if (a.w_bit == 4) return f16 ? launch_large<4, XF16>(a, p) : launch_large<4, XBF16>(a, p);
     return f16 ? launch_large<2, XF16>(a, p) : launch_large<2, XBF16>(a, p);

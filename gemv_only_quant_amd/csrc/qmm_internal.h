@@ -50,6 +50,10 @@ struct GemvLowbitPlan {
 GemvLowbitPlan plan_gemv_lowbit(int M, int N, int K, int w_bit, int group_size);
 hipError_t launch_gemv_lowbit(const MatmulArgs& a, const GemvLowbitPlan& p);
 
+// ---- low-bit GEMV on the tile layout (qmm_gemm, small M) ----------------
+constexpr int kGemvTileMaxM = 4;
+hipError_t launch_gemv_tile(const MatmulArgs& a);
+
 // ---- int8 GEMV on (N, K) int8 ------------------------------------------
 struct GemvInt8Plan {
   int mb;        // M bucket
@@ -70,7 +74,8 @@ hipError_t launch_dequant(const void* Q, int layout, const void* scales, const v
 
 // ---- MFMA GEMM on the tile layout ---------------------------------------
 struct GemmPlan {
-  int kind;      // 0: skinny (registers-direct, K split over the waves), 1: large-M tiled
+  int kind;      // 0: skinny (registers-direct, K split over the waves), 1: large-M tiled,
+                 // 2: VALU GEMV on the tile layout (small M, low-bit)
   int mtile;     // rows per M tile
   int nt;        // 16-column strips per workgroup (skinny)
   int waves;     // waves per workgroup, splitting K (skinny: 4 or 8)

@@ -127,7 +127,58 @@ def test_workspace_reused_across_calls():
         assert_within_bound(y[ms, ns], y_ref, a_ref, f"call {i}")
 
 
-FULL = ["int8_skinny_m16_k4096_n14336", "int8_skinny_m32_k4096_n14336",
+# ------------------------------------------ decode GEMV on the tile layout
+# qmm_gemm at M <= 2 (int2: M <= 4) runs the VALU GEMV that reads each strip as
+# one contiguous run: passes of 32 or 16 blocks (int4) / 16 blocks (int2)
+TILE = [  # M, N, K, w_bit, group, x_dtype, symmetric
+    (1, 16, 128, 4, 128, si.F16, False),       # one block: waves 1-3 idle
+    (1, 4096, 4096, 4, 128, si.F16, False),    # the headline shape
+    (1, 48, 4224, 4, 64, si.BF16, False),      # 33 blocks: a second pass of one block
+    (2, 64, 8192, 4, 32, si.F16, True),        # two passes, g32 (4 groups per block)
+    (2, 80, 1024, 4, 256, si.BF16, False),     # 8 blocks (passes of 16), a group over two
+    (2, 128, 12288, 4, 128, si.F16, False),    # three passes
+    (3, 64, 2048, 2, 64, si.F16, False),       # int2, M bucket 4
+    (1, 32, 2048, 2, 64, si.BF16, False),      # int2, 4 groups per block
+    (2, 16, 8448, 2, 32, si.F16, False),       # int2, 33 blocks, 8 groups per block
+    (4, 48, 4096, 2, 128, si.BF16, True),      # int2 at M 4 (16 blocks per pass)
+    (1, 16, 512, 2, 256, si.F16, False),
+]
+
+
+@pytest.mark.parametrize("M,N,K,w_bit,gs,xdt,sym", TILE)
+def test_gemm_decode_tile_within_bound(M, N, K, w_bit, gs, xdt, sym):
+    case = si.lowbit_case(M, N, K, w_bit, gs, xdt, sym, seed=40 + M + N + K + w_bit)
+    y = run_gemm(case)
+    y_ref, a_ref = oracle.qmm(*case.oracle_args())
+    assert_within_bound(y, y_ref, a_ref, f"tile gemv w{w_bit} M{M} N{N} K{K} g{gs}")
+
+
+@pytest.mark.parametrize("M,N,K,w_bit,gs,sym", [(1, 64, 4096, 4, 128, False),
+                                                 (2, 32, 4224, 4, 32, True),
+                                                 (2, 48, 8192, 2, 64, False),
+                                                 (4, 16, 2048, 2, 256, False)])
+@pytest.mark.parametrize("xdt", [si.F16, si.BF16])
+def test_gemm_decode_tile_exact_probe_bit_exact(M, N, K, w_bit, gs, sym, xdt):
+    case = si.exact_lowbit_case(M, N, K, w_bit, gs, xdt, sym, seed=M * 5 + K)
+    y = run_gemm(case)
+    y_ref, _ = oracle.qmm(*case.oracle_args())
+    assert np.array_equal(y.astype(np.float64), y_ref)
+
+
+def test_gemm_decode_tile_one_hot_reproduces_weights():
+    """x = e_k, one row per k (M = 4 rows per call): y reads W back exactly."""
+    M, N, K = 4, 32, 512
+    base = si.lowbit_case(M, N, K, 4, 64, si.F16, False, seed=43)
+    W = oracle.dequant(base.np_Q(), base.np_scales(), base.np_zeros(), N, K, 4, 64)
+    for ks in ([0, 1, 7, 8], [31, 32, 127, 128], [129, 255, 300, 511]):
+        case = si.one_hot(base, ks)
+        y = run_gemm(case)
+        for m, k in enumerate(ks):
+            assert np.array_equal(y[m], W[k]), k
+
+
+FULL = ["int4_g128_asym_gemv_m1_k4096_n4096", "int4_pc_sym_gemv_m1_k4096_n4096",
+        "int8_skinny_m16_k4096_n14336", "int8_skinny_m32_k4096_n14336",
         "int8_skinny_m64_k4096_n14336", "int4_g128_sym_m16_k8192_n8192",
         "int4_g128_asym_smalln_m16_k14336_n1024",
         "int4_g128_asym_prefill_m4096_k4096_n11008", "int2_g64_asym_prefill_m4096_k4096_n11008"]
@@ -194,14 +245,15 @@ def test_gemm_large_one_hot_reproduces_weights():
 
 
 # ------------------------------------ small N, long K: K split over workgroups
-# Shapes whose tiles alone leave most CUs idle.  With a workspace, K is split
+# Shapes whose tiles alone leave most CUs idle (M >= 5: smaller low-bit
+# batches take the decode GEMV above).  With a workspace, K is split
 # over several workgroups per tile and the last to arrive adds the partials;
 # with a NULL workspace the planner gives each workgroup 8 waves instead
 # (>= 16 stages of K), so both plans are checked on the same shapes.
 MANYWAVES = [  # M, N, K, w_bit, group, x_dtype, symmetric
     (16, 64, 4096, 4, 128, si.F16, False),      # 4 tiles, 32 stages
-    (3, 256, 8192, 4, 64, si.BF16, False),      # ragged M
-    (1, 32, 6144, 4, 256, si.F16, True),        # 48 stages: uneven shares
+    (5, 256, 8192, 4, 64, si.BF16, False),      # ragged M
+    (6, 32, 6144, 4, 256, si.F16, True),        # 48 stages: uneven shares
     (16, 80, 5120, 4, 32, si.BF16, False),      # 40 stages, g32
     (30, 48, 4096, 4, 128, si.F16, False),      # two 16-row tiles
     (16, 48, 8192, 2, 64, si.BF16, False),      # int2
@@ -246,8 +298,8 @@ def test_split_workspace_rearmed_over_calls():
     tile and split counts): each result is right, and after every call the
     tickets are back at zero."""
     ws = torch.zeros(16 << 20, dtype=torch.uint8, device="cuda")
-    shapes = [(16, 64, 4096, 4, 128), (16, 1024, 14336, 4, 128), (3, 32, 8192, 2, 64),
-              (16, 64, 4096, 4, 128), (40, 48, 4096, 8, 0), (1, 16, 2048, 4, 128)]
+    shapes = [(16, 64, 4096, 4, 128), (16, 1024, 14336, 4, 128), (7, 32, 8192, 2, 64),
+              (16, 64, 4096, 4, 128), (40, 48, 4096, 8, 0), (5, 16, 2048, 4, 128)]
     for i, (M, N, K, wb, gs) in enumerate(shapes):
         need = qmm.qmm_workspace_bytes(M, N, K, wb, gs)
         assert 0 < need <= ws.numel(), (M, N, K, need)
