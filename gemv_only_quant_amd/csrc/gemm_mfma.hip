@@ -19,6 +19,7 @@
 //        y += s * (acc - (B + z) * xsum)
 //    in fp32 -- so the matrix cores only see exact integers and the group
 //    scale is applied once per group (the page's w = (q - z) * s, regrouped).
+#include <algorithm>
 #include <type_traits>
 
 #include "qmm_device.h"
@@ -476,12 +477,11 @@ template <> __device__ __forceinline__ void mfma16_acc<XBF16>(f32x4_t& c, const 
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
 }
 
-// 16-row tiles per wave in the large-M kernel (rows per workgroup / 16):
-// 16 (one wave per SIMD, 256 accumulators) or 8 (two waves per SIMD).
-static int large_mt() {
-  static const int e = env_int("QMM_LARGE_MT");
-  return (e == 8 || e == 16) ? e : 16;
-}
+// 16-row tiles per workgroup in the large-M kernel (256 rows: one wave per
+// SIMD, 256 fp32 accumulators per lane).
+constexpr int kLargeMT = 16;
+// eighths of a stage's row tiles over which its loads are issued
+constexpr int kLoadSpan = 4;
 
 // s_waitcnt with vmcnt = 0 and the other counters at their maximum.
 static constexpr int kWaitVm0 = 0x0F70;
@@ -508,7 +508,8 @@ struct GroupConst {
 };
 
 template <int W_BIT, int XDT>
-__device__ __forceinline__ uint32_t bpair_scaled(uint32_t w, int h, int t, const GroupConst& g) {
+__device__ __forceinline__ uint32_t bpair_scaled(uint32_t w, int h, int t, const GroupConst& g,
+                                              uint32_t hi_bits) {
   if constexpr (W_BIT == 4 && XDT == XBF16) {
     // Fields t = 1, 3 are taken where they sit, at bits 4-7 of each half:
     // OR-ed under the fp16 1024 pattern they read 1024 + 16 q, and
@@ -517,7 +518,7 @@ __device__ __forceinline__ uint32_t bpair_scaled(uint32_t w, int h, int t, const
     // by 8 serves fields 2 and 3, so a word costs one shift and four
     // mask-ors instead of three shifts.  Same bits out as the plain path.
     const uint32_t v = t >= 2 ? w >> 8 : w;
-    const uint32_t m = (v & ((t & 1) ? 0x00F000F0u : 0x000F000Fu)) | 0x64006400u;
+    const uint32_t m = (v & ((t & 1) ? 0x00F000F0u : 0x000F000Fu)) | hi_bits;
     const half2_t mh = __builtin_bit_cast(half2_t, m);
     const float sc = (t & 1) ? g.s16 : g.s;
     const float zb = (t & 1) ? g.zb16_s : g.zb_s;
@@ -528,7 +529,7 @@ __device__ __forceinline__ uint32_t bpair_scaled(uint32_t w, int h, int t, const
   }
   constexpr uint32_t FIELD2 = W_BIT == 4 ? 0x000F000Fu : 0x00030003u;
   const int sh = W_BIT == 4 ? 4 * t : 2 * (4 * h + t);
-  const uint32_t m = ((w >> sh) & FIELD2) | 0x64006400u;
+  const uint32_t m = ((w >> sh) & FIELD2) | hi_bits;
   const half2_t mh = __builtin_bit_cast(half2_t, m);
   if constexpr (XDT == XBF16) {
     const float lo = __builtin_fmaf((float)mh[0], g.s, -g.zb_s);
@@ -541,14 +542,126 @@ __device__ __forceinline__ uint32_t bpair_scaled(uint32_t w, int h, int t, const
   }
 }
 
-template <int W_BIT, int XDT, int GS, bool ZP, int MT>
-__global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
+// Inputs of one operand register (the bpair_scaled recipes).  bf16: the word
+// shifted so that its two codes sit under `mask`, and the fp32 scale and
+// bias product that turn the fp16 1024 + c (or 1024 + 16 c) into (c - z) * s.
+//   fp16: the word shifted to its two codes, and the pairs -(1024 + z) and
+//   s (v_pk_add_f16 then v_pk_mul_f16, the bpair_scaled fp16 recipe).
+struct BSrc {
+  uint32_t v, mask;
+  uint32_t p, q;  // bf16: scale and bias product (fp32 bits); fp16: -(1024 + z) and s pairs
+};
+template <int W_BIT, int XDT>
+__device__ __forceinline__ BSrc bsrc(uint32_t w, int h, int t, const GroupConst& g) {
+  if constexpr (XDT == XBF16) {
+    if constexpr (W_BIT == 4) {
+      const float sc = (t & 1) ? g.s16 : g.s, zb = (t & 1) ? g.zb16_s : g.zb_s;
+      return {t >= 2 ? w >> 8 : w, (t & 1) ? 0x00F000F0u : 0x000F000Fu,
+              __builtin_bit_cast(uint32_t, sc), __builtin_bit_cast(uint32_t, zb)};
+    } else {
+      return {w >> (2 * (4 * h + t)), 0x00030003u, __builtin_bit_cast(uint32_t, g.s),
+              __builtin_bit_cast(uint32_t, g.zb_s)};
+    }
+  } else {
+    if constexpr (W_BIT == 4) return {w >> (4 * t), 0x000F000Fu, g.nzb_h2, g.s_h2};
+    else return {w >> (2 * (4 * h + t)), 0x00030003u, g.nzb_h2, g.s_h2};
+  }
+}
+
+// The NT MFMAs of one row tile (bf16) with one operand register of a later
+// k step made between them: mask-or, the two mixed-precision FMAs, the
+// rounding to a bf16 pair -- each issues while an MFMA runs instead of
+// waiting behind the row tile's MFMAs.  One asm block, because the
+// scheduler does not see the accumulator-pinned MFMAs as MFMAs.  No
+// hazards inside: the conversion writes only its own (early-clobber)
+// registers, none of which an MFMA here reads.
+__device__ __forceinline__ uint32_t mfma_row_deq(f32x4_t (&c)[4], const u32x4_t& a,
+                                                 const u32x4_t (&b)[4], const BSrc& src,
+                                                 uint32_t hi_bits) {
+  uint32_t out, m;
+  float lo, up;
+  asm volatile(
+      "v_mfma_f32_16x16x32_bf16 %[c0], %[a], %[b0], %[c0]\n\t"
+      "v_and_or_b32 %[m], %[v], %[mask], %[hi]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c1], %[a], %[b1], %[c1]\n\t"
+      "v_fma_mix_f32 %[lo], %[m], %[sc], -%[zb] op_sel_hi:[1,0,0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c2], %[a], %[b2], %[c2]\n\t"
+      "v_fma_mix_f32 %[up], %[m], %[sc], -%[zb] op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c3], %[a], %[b3], %[c3]\n\t"
+      "v_cvt_pk_bf16_f32 %[out], %[lo], %[up]"
+      : [c0] "+a"(c[0]), [c1] "+a"(c[1]), [c2] "+a"(c[2]), [c3] "+a"(c[3]), [out] "=&v"(out),
+        [m] "=&v"(m), [lo] "=&v"(lo), [up] "=&v"(up)
+      : [a] "v"(a), [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]),
+        [v] "v"(src.v), [mask] "s"(src.mask), [hi] "v"(hi_bits), [sc] "v"(src.p),
+        [zb] "v"(src.q));
+  return out;
+}
+__device__ __forceinline__ uint32_t mfma_row_deq(f32x4_t (&c)[3], const u32x4_t& a,
+                                                 const u32x4_t (&b)[3], const BSrc& src,
+                                                 uint32_t hi_bits) {
+  uint32_t out, m;
+  float lo, up;
+  asm volatile(
+      "v_mfma_f32_16x16x32_bf16 %[c0], %[a], %[b0], %[c0]\n\t"
+      "v_and_or_b32 %[m], %[v], %[mask], %[hi]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c1], %[a], %[b1], %[c1]\n\t"
+      "v_fma_mix_f32 %[lo], %[m], %[sc], -%[zb] op_sel_hi:[1,0,0]\n\t"
+      "v_mfma_f32_16x16x32_bf16 %[c2], %[a], %[b2], %[c2]\n\t"
+      "v_fma_mix_f32 %[up], %[m], %[sc], -%[zb] op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "v_cvt_pk_bf16_f32 %[out], %[lo], %[up]"
+      : [c0] "+a"(c[0]), [c1] "+a"(c[1]), [c2] "+a"(c[2]), [out] "=&v"(out), [m] "=&v"(m),
+        [lo] "=&v"(lo), [up] "=&v"(up)
+      : [a] "v"(a), [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [v] "v"(src.v),
+        [mask] "s"(src.mask), [hi] "v"(hi_bits), [sc] "v"(src.p), [zb] "v"(src.q));
+  return out;
+}
+
+// fp16: mask-or, (1024 + q) - (1024 + z) exact, times s rounded once.
+__device__ __forceinline__ uint32_t mfma_row_deq_f16(f32x4_t (&c)[4], const u32x4_t& a,
+                                                     const u32x4_t (&b)[4], const BSrc& src,
+                                                     uint32_t hi_bits) {
+  uint32_t out, m, d;
+  asm volatile(
+      "v_mfma_f32_16x16x32_f16 %[c0], %[a], %[b0], %[c0]\n\t"
+      "v_and_or_b32 %[m], %[v], %[mask], %[hi]\n\t"
+      "v_mfma_f32_16x16x32_f16 %[c1], %[a], %[b1], %[c1]\n\t"
+      "v_pk_add_f16 %[d], %[m], %[nz]\n\t"
+      "v_mfma_f32_16x16x32_f16 %[c2], %[a], %[b2], %[c2]\n\t"
+      "v_pk_mul_f16 %[out], %[d], %[sh]\n\t"
+      "v_mfma_f32_16x16x32_f16 %[c3], %[a], %[b3], %[c3]"
+      : [c0] "+a"(c[0]), [c1] "+a"(c[1]), [c2] "+a"(c[2]), [c3] "+a"(c[3]), [out] "=&v"(out),
+        [m] "=&v"(m), [d] "=&v"(d)
+      : [a] "v"(a), [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [b3] "v"(b[3]),
+        [v] "v"(src.v), [mask] "s"(src.mask), [hi] "v"(hi_bits), [nz] "v"(src.p),
+        [sh] "v"(src.q));
+  return out;
+}
+__device__ __forceinline__ uint32_t mfma_row_deq_f16(f32x4_t (&c)[3], const u32x4_t& a,
+                                                     const u32x4_t (&b)[3], const BSrc& src,
+                                                     uint32_t hi_bits) {
+  uint32_t out, m, d;
+  asm volatile(
+      "v_mfma_f32_16x16x32_f16 %[c0], %[a], %[b0], %[c0]\n\t"
+      "v_and_or_b32 %[m], %[v], %[mask], %[hi]\n\t"
+      "v_mfma_f32_16x16x32_f16 %[c1], %[a], %[b1], %[c1]\n\t"
+      "v_pk_add_f16 %[d], %[m], %[nz]\n\t"
+      "v_mfma_f32_16x16x32_f16 %[c2], %[a], %[b2], %[c2]\n\t"
+      "v_pk_mul_f16 %[out], %[d], %[sh]"
+      : [c0] "+a"(c[0]), [c1] "+a"(c[1]), [c2] "+a"(c[2]), [out] "=&v"(out), [m] "=&v"(m),
+        [d] "=&v"(d)
+      : [a] "v"(a), [b0] "v"(b[0]), [b1] "v"(b[1]), [b2] "v"(b[2]), [v] "v"(src.v),
+        [mask] "s"(src.mask), [hi] "v"(hi_bits), [nz] "v"(src.p), [sh] "v"(src.q));
+  return out;
+}
+
+template <int W_BIT, int XDT, int GS, bool ZP, int NT>
+__global__ __launch_bounds__(256, 1) void gemm_large_kernel(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ Qt,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qz, void* __restrict__ y,
-    int M, int N, int K, int tile_opts) {
+    int M, int N, int K, int tile_opts, int strip0) {
   const int n_tiles = tiles_of(tile_opts), ydt = ydt_of(tile_opts), gmask = gmask_of(tile_opts);
-  constexpr int BM = 16 * MT;          // rows per workgroup (MT 16-row tiles)
-  constexpr int NT = 4;                 // strips per wave
+  constexpr int MT = kLargeMT;          // 16-row tiles per workgroup
+  constexpr int BM = 16 * MT;           // rows per workgroup
   constexpr int KS = 128;               // k per stage
   constexpr int STEPS = KS / 32;        // MFMA k steps per stage
   constexpr int KB = W_BIT == 4 ? 128 : 256;  // layout block depth
@@ -560,22 +673,37 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
 
   __shared__ u32x4_t xa[2][FRAGS * 64];
 
+  // fp16 1024 in both halves, held in a register: mask-and-or of the codes
+  // is then one v_and_or_b32 (an instruction takes one literal at most)
+  uint32_t hi_bits;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(hi_bits));
+
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, quad = lane >> 4;
   const int w = xcd_remap(blockIdx.x, gridDim.x);
   const int nt = w % n_tiles, mt_idx = w / n_tiles;
   const int m0 = mt_idx * BM;
   const int strips = N / 16;
-  const int s0 = (nt * 4 + wave) * NT;
+  const int s0 = strip0 + (nt * 4 + wave) * NT;  // this wave's first strip
   const int nblk = K / KB;
   const int nst = K / KS;
 
-  // Loads always use a valid strip (the last one stands in for strips past
-  // N); their results are simply not stored.
-  int sidx[NT];
-#pragma unroll
-  for (int s = 0; s < NT; ++s) sidx[s] = min(s0 + s, strips - 1);
+  // Every load goes through a buffer descriptor whose range ends where the
+  // operand does: rows past M and strips past N read zeros (they only feed
+  // outputs that are never stored), and each address is a per-lane offset
+  // fixed for the whole K loop plus a wave-uniform offset for the stage.
+  //   x: the workgroup's rows; weights: the wave's strips (1 KiB blocks,
+  //   strip-major); scales / zero words: from the wave's first column on.
+  const int sc0 = min(s0, strips);
+  const int nvalid = min(NT, strips - sc0);
+  const int G = gmask != 0 ? K / GS : 1;
+  const buf_t xb = make_buf(x + (size_t)m0 * K, (uint32_t)(min(BM, M - m0) * K * 2));
+  const buf_t qb = make_buf(Qt + (size_t)sc0 * nblk * 64, (uint32_t)(nvalid * nblk * 1024));
+  const buf_t sb = make_buf(scales + 16 * sc0, (uint32_t)(((size_t)G * N - 16 * sc0) * 2));
+  const buf_t zb = make_buf(qz + 16 * sc0,
+                            ZP ? (uint32_t)(((size_t)((G + PACK - 1) / PACK) * N - 16 * sc0) * 4)
+                               : 0u);
 
   // The x tile of a stage is stored by row tile: 16 rows x 16 chunks of 16
   // bytes (the stage's 128 k of a row), chunk c of row r at slot 16 r +
@@ -586,64 +714,78 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
   // contiguous bytes each; the fragment-order alternative, 16 rows x 64
   // bytes per load, is served at well under half the rate).  A fragment
   // (row l16, chunk 4 kk + quad) is then one conflict-free ds_read_b128.
-  // Each wave moves FRAGS / 4 units straight from global memory into LDS.
-  // Rows past M read row M - 1 instead: they only feed output rows that are
-  // never stored.
+  // Each wave moves FRAGS / 4 units straight from memory into LDS (buffer
+  // loads to LDS: the destination is a wave-uniform LDS address, lane p
+  // writing 16 bytes at + 16 p).
   static_assert(KS == 128 && STEPS == 4, "x tile layout: 16 chunks per row, 4 loads per row tile");
-  const int rows_left = M - 1 - m0;
-  auto x_unit = [&](int f, int sx, int buf) {
-    const int r = 4 * (f % 4) + quad;
-    const int rr = min(16 * (f / 4) + r, rows_left);
-    const int k = sx * KS + 8 * (l16 ^ r);
-    __builtin_amdgcn_global_load_lds(
-        (const void*)(x + (size_t)(m0 + rr) * K + k),
-        (__attribute__((address_space(3))) void*)(&xa[buf][f * 64]), 16, 0, 0);
+  static_assert(MT % 4 == 0, "a wave's load units cover whole row-tile quarters");
+  int xo[4];  // lane byte offset for units with f % 4 = c
+#pragma unroll
+  for (int c = 0; c < 4; ++c) xo[c] = (quad * K + 8 * (l16 ^ (4 * c + quad))) * 2;
+  auto x_unit = [&](int j, int sx, int buf) {
+    const int f = wave * (FRAGS / 4) + j;
+    const int row = 16 * (f / 4) + 4 * (j % 4);  // first of the unit's 4 rows
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        xb, (__attribute__((address_space(3))) void*)(&xa[buf][f * 64]), 16, xo[j % 4],
+        (row * K + sx * KS) * 2, 0, 0);
   };
   auto load_x = [&](int st, int buf) {
 #pragma unroll
-    for (int j = 0; j < FRAGS / 4; ++j) x_unit(wave * (FRAGS / 4) + j, st, buf);
+    for (int j = 0; j < FRAGS / 4; ++j) x_unit(j, st, buf);
   };
 
+  // a stage's words of a strip: int4 the lane's whole 16-byte slot of the
+  // 128-deep block; int2 the half (8 bytes) of the 256-deep block's slot
+  // that holds the stage's 128 k
+  using Slot = typename std::conditional<W_BIT == 4, u32x4_t, u32x2_t>::type;
   struct WRegs {
-    u32x4_t slot[NT];
+    Slot slot[NT];
     uint32_t sc[NT][NGS];
     uint32_t zw[NT];
   };
-  auto load_w = [&](int st, WRegs& R) {
+  const int qv = lane * 16, sv = l16 * 2, zv = l16 * 4;
+  auto load_slot = [&](int s, int st, WRegs& R) {
     const int kb = (st * KS) / KB;
-    const int g0 = (st * KS) / GS;
+    if constexpr (W_BIT == 4)
+      R.slot[s] = __builtin_amdgcn_raw_buffer_load_b128(qb, qv, (s * nblk + kb) * 1024, 0);
+    else
+      R.slot[s] = __builtin_amdgcn_raw_buffer_load_b64(qb, qv, (s * nblk + kb) * 1024 + 8 * (st & 1), 0);
+  };
+  auto load_scale = [&](int s, int q, int st, WRegs& R) {
+    const int g = ((st * KS) / GS + q) & gmask;
+    R.sc[s][q] = __builtin_amdgcn_raw_buffer_load_b16(sb, sv + 32 * s, g * N * 2, 0);
+  };
+  auto load_zero = [&](int s, int st, WRegs& R) {
+    if constexpr (ZP) {
+      const int g = ((st * KS) / GS) & gmask;
+      R.zw[s] = __builtin_amdgcn_raw_buffer_load_b32(zb, zv + 64 * s, (g / PACK) * N * 4, 0);
+    } else {
+      R.zw[s] = ZSYM;
+    }
+  };
+  auto load_w = [&](int st, WRegs& R) {
 #pragma unroll
     for (int s = 0; s < NT; ++s) {
-      R.slot[s] = Qt[((size_t)sidx[s] * nblk + kb) * 64 + lane];
-      const int n = 16 * sidx[s] + l16;
+      load_slot(s, st, R);
 #pragma unroll
-      for (int q = 0; q < NGS; ++q) R.sc[s][q] = scales[(size_t)((g0 + q) & gmask) * N + n];
-      if constexpr (ZP) R.zw[s] = qz[(size_t)((g0 & gmask) / PACK) * N + n];
-      else R.zw[s] = ZSYM;
+      for (int q = 0; q < NGS; ++q) load_scale(s, q, st, R);
+      load_zero(s, st, R);
     }
   };
   // Loads issued during a stage, one at a time: j < NWL are weight-side
   // (slots, then scales, then zero words) of stage sw, the rest this wave's
-  // x fragments of stage sx.  The k loop issues them spread over its row
-  // tiles: a wave issues in order, so a burst of loads at the top of a stage
-  // would hold its MFMAs back until the memory pipeline had taken them all.
+  // x fragments of stage sx.  The k loop issues them spread over its first
+  // row tiles: a wave issues in order, so a burst of loads at the top of a
+  // stage would hold its MFMAs back until the memory pipeline had taken
+  // them all; what is issued late in the stage has little time left to land
+  // before the stage's closing wait.
   constexpr int NWL = NT * (2 + NGS);
   constexpr int NLD = NWL + FRAGS / 4;
   auto load_part = [&](int j, int sw, int sx, int buf, WRegs& R) {
-    const int kb = (sw * KS) / KB;
-    const int g0 = (sw * KS) / GS;
-    if (j < NT) {
-      R.slot[j] = Qt[((size_t)sidx[j] * nblk + kb) * 64 + lane];
-    } else if (j < NT + NT * NGS) {
-      const int s = (j - NT) / NGS, q = (j - NT) % NGS;
-      R.sc[s][q] = scales[(size_t)((g0 + q) & gmask) * N + 16 * sidx[s] + l16];
-    } else if (j < NWL) {
-      const int s = j - NT - NT * NGS;
-      if constexpr (ZP) R.zw[s] = qz[(size_t)((g0 & gmask) / PACK) * N + 16 * sidx[s] + l16];
-      else R.zw[s] = ZSYM;
-    } else {
-      x_unit(wave * (FRAGS / 4) + (j - NWL), sx, buf);
-    }
+    if (j < NT) load_slot(j, sw, R);
+    else if (j < NT + NT * NGS) load_scale((j - NT) / NGS, (j - NT) % NGS, sw, R);
+    else if (j < NWL) load_zero(j - NT - NT * NGS, sw, R);
+    else x_unit(j - NWL, sx, buf);
   };
 
   f32x4_t acc[MT][NT];
@@ -658,23 +800,24 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
     const int g0 = (sa * KS) / GS;
 #pragma unroll
     for (int q = 0; q < NGS; ++q) {
-      const uint32_t sb = R.sc[s][q] & 0xFFFFu;
-      const float sc = f16_bits_to_f32((uint16_t)sb);
+      const uint32_t sbits = R.sc[s][q] & 0xFFFFu;
+      const float sc = f16_bits_to_f32((uint16_t)sbits);
       const uint32_t z = (R.zw[s] >> ((((g0 + q) & gmask) % PACK) * W_BIT)) & ((1u << W_BIT) - 1u);
-      const float zb = 1024.0f + (float)z;
+      const float zbias = 1024.0f + (float)z;
       g[q].s = sc;
-      g[q].zb_s = zb * sc;
+      g[q].zb_s = zbias * sc;
       g[q].s16 = sc * 0.0625f;
       g[q].zb16_s = (64.0f + (float)z) * sc;
-      g[q].s_h2 = sb | (sb << 16);
-      const uint32_t nzb = __builtin_bit_cast(uint16_t, (_Float16)(-zb));
+      g[q].s_h2 = sbits | (sbits << 16);
+      const uint32_t nzb = __builtin_bit_cast(uint16_t, (_Float16)(-zbias));
       g[q].nzb_h2 = nzb | (nzb << 16);
     }
   };
   // layout word of k step kk of a stage (int4: one word per step; int2: one
   // per two steps, the stage being half `sub` of a 256-deep block)
   auto word_of = [&](const WRegs& R, int s, int sub, int kk) {
-    return W_BIT == 4 ? R.slot[s][kk] : R.slot[s][(STEPS * sub + kk) >> 1];
+    (void)sub;
+    return W_BIT == 4 ? R.slot[s][kk] : R.slot[s][kk >> 1];
   };
 
   // Weight registers of three stages: the current one, the next (loaded
@@ -704,13 +847,14 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
   // The first stage's group constants and first B fragment are made here;
   // from then on each stage makes the next one's during its last k step,
   // so a stage opens straight into its MFMAs.
-  GroupConst gc[NT][NGS], gcn[NT][NGS];
+  GroupConst gc[NT][NGS];
   u32x4_t b[NT], bn[NT];
 #pragma unroll
   for (int s = 0; s < NT; ++s) {
     group_consts(cur, 0, s, gc[s]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) b[s][t] = bpair_scaled<W_BIT, XDT>(word_of(cur, s, 0, 0), 0, t, gc[s][0]);
+    for (int t = 0; t < 4; ++t)
+      b[s][t] = bpair_scaled<W_BIT, XDT>(word_of(cur, s, 0, 0), 0, t, gc[s][0], hi_bits);
   }
   for (int st = 0; st < nst; ++st) {
     const int buf = st & 1;
@@ -725,12 +869,12 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
 
     // Software pipeline inside the stage: while the NT MFMAs of row tile i of
     // k step k run, (1) the A fragment two tiles ahead is read from LDS,
-    // (2) one operand register of the next k step's B fragments is
-    // dequantized (MT row tiles x 1 register = NT strips x 4 registers when
-    // MT = 16) -- in the last k step those of the next stage, after its
-    // group constants -- and (3) part of the next stage's loads is issued.
-    // The scheduling barriers hold this interleave; without them the
-    // compiler hoists every read and every conversion (and spills).
+    // (2) part of the next k step's B fragments is dequantized (the NT x 4
+    // operand registers spread over the MT row tiles) -- in the last k step
+    // those of the next stage, after its group constants -- and (3) part of
+    // the next stage's loads is issued.  The scheduling barriers hold this
+    // interleave; without them the compiler hoists every read and every
+    // conversion (and spills).
     // fragment (row tile i, k step kk) = slot 256 i + 16 l16 + ((4 kk + quad) ^ l16)
     auto afrag = [&](int i, int kk) { return xs_buf[256 * i + 16 * l16 + ((4 * kk + quad) ^ l16)]; };
     u32x4_t a0 = afrag(0, 0);
@@ -744,28 +888,34 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
         const int t2 = k * MT + i + 2;  // fragment two ahead, in (k, i) order
         u32x4_t an = a1;
         if (t2 < STEPS * MT) an = afrag(t2 % MT, t2 / MT);
-#pragma unroll
-        for (int s = 0; s < NT; ++s) mfma16_acc<XDT>(acc[i][s], a0, b[s]);
-        if (kn < STEPS) {
-#pragma unroll
-          for (int r = i * NT * 4 / MT; r < (i + 1) * NT * 4 / MT; ++r)
-            bn[r / 4][r % 4] = bpair_scaled<W_BIT, XDT>(word_of(cur, r / 4, sub, kn),
-                                                        (STEPS * sub + kn) & 1, r % 4, gc[r / 4][qn]);
+        // this row tile's operand register of the next k step (of the next
+        // stage in the last k step), made between its MFMAs
+        const int r0 = i * NT * 4 / MT, r1 = (i + 1) * NT * 4 / MT;
+        static_assert(NT * 4 <= MT, "one operand register per row tile at most");
+        // (the last k step makes the next stage's group constants in place:
+        // this stage's are no longer read by then)
+        if (kn == STEPS && i < NT) group_consts(nx1, stn, i, gc[i]);
+        if (r0 < r1) {
+          const int r = r0;
+          const BSrc src =
+              kn < STEPS ? bsrc<W_BIT, XDT>(word_of(cur, r / 4, sub, kn), (STEPS * sub + kn) & 1,
+                                            r % 4, gc[r / 4][qn])
+                         : bsrc<W_BIT, XDT>(word_of(nx1, r / 4, subn, 0), (STEPS * subn) & 1,
+                                            r % 4, gc[r / 4][0]);
+          if constexpr (XDT == XBF16) bn[r / 4][r % 4] = mfma_row_deq(acc[i], a0, b, src, hi_bits);
+          else bn[r / 4][r % 4] = mfma_row_deq_f16(acc[i], a0, b, src, hi_bits);
         } else {
-          if (i < NT) group_consts(nx1, stn, i, gcn[i]);
 #pragma unroll
-          for (int r = i * NT * 4 / MT; r < (i + 1) * NT * 4 / MT; ++r)
-            bn[r / 4][r % 4] = bpair_scaled<W_BIT, XDT>(word_of(nx1, r / 4, subn, 0),
-                                                        (STEPS * subn) & 1, r % 4, gcn[r / 4][0]);
+          for (int s = 0; s < NT; ++s) mfma16_acc<XDT>(acc[i][s], a0, b[s]);
         }
-        // this row tile's share of the loads, spread over the first 7/8 of
-        // the row tiles
+        // this row tile's share of the loads, spread over the first
+        // kLoadSpan eighths of the row tiles
         {
-          constexpr int S7 = 7 * STEPS * MT / 8;
-          static_assert(NLD <= 2 * S7, "two loads per row tile at most");
+          constexpr int SPAN = kLoadSpan * STEPS * MT / 8;
+          static_assert(NLD <= 2 * SPAN, "two loads per row tile at most");
           const int p = k * MT + i;
-          const int j0 = (p * NLD + S7 - 1) / S7;
-          const int j1 = min(NLD, ((p + 1) * NLD + S7 - 1) / S7);
+          const int j0 = (p * NLD + SPAN - 1) / SPAN;
+          const int j1 = min(NLD, ((p + 1) * NLD + SPAN - 1) / SPAN);
           if (j0 < j1) load_part(j0, stw, stn, buf ^ 1, nx2);
           if (j0 + 1 < j1) load_part(j0 + 1, stw, stn, buf ^ 1, nx2);
         }
@@ -778,10 +928,6 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
     }
     cur = nx1;
     nx1 = nx2;
-#pragma unroll
-    for (int s = 0; s < NT; ++s)
-#pragma unroll
-      for (int q = 0; q < NGS; ++q) gc[s][q] = gcn[s][q];
     // the next stage's x tile was written to LDS by the memory pipeline:
     // wait for this wave's loads, then for every wave's
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -800,7 +946,7 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
     for (int s = 0; s < NT; ++s) asm volatile("" : "+a"(acc[i][s]));
   __builtin_amdgcn_sched_barrier(0);
 
-  // y goes out through LDS, one 16-row tile at a time: the wave's 16 x 64
+  // y goes out through LDS, one 16-row tile at a time: the wave's 16 x 16 NT
   // block is written row-major into its own LDS region (row stride 68
   // floats: both the column-wise writes and the row-wise reads hit 64
   // distinct banks), then read back so that each store instruction covers
@@ -813,7 +959,7 @@ __global__ __launch_bounds__(256, MT <= 8 ? 2 : 1) void gemm_large_kernel(
   // region needs no barrier between tiles.
   float* const yl = reinterpret_cast<float*>(&xa[0][0]) + wave * (16 * 68);
   const int prow = lane >> 4, pcol = 4 * (lane & 15);  // row within 4, first column
-  const bool pcol_ok = s0 + ((lane & 15) >> 2) < strips;
+  const bool pcol_ok = (lane & 15) < 4 * NT && s0 + ((lane & 15) >> 2) < strips;
   with_y(y, ydt, [&](auto* yt) {
     using T = typename std::remove_pointer<decltype(yt)>::type;
 #pragma unroll
@@ -854,15 +1000,60 @@ static void skinny_shape(int M, int N, int* mt, int* nt) {
   if (want == 1 || want == 2 || want == 4) *nt = want;
 }
 
+// Compute units of the current device (256 on MI355X), read once per device.
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        v <= 0)
+      v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+// Large-M column split.  A workgroup (one per CU) takes full tiles of 16
+// strips (4 waves x 4) or narrow tiles of 12 strips (4 waves x 3), each over
+// all K; the workgroups of one launch run in rounds of `cus`.  Full tiles
+// cover the first n_full column tiles, narrow ones the rest, launched after
+// them: of the splits, the one with the least estimated time -- rounds of
+// full tiles plus rounds of narrow ones, a narrow round costing kNarrowCost
+// of a full one (3 of 4 strips' MFMAs; the x tile is loaded whole either
+// way).  At M = 4096, N = 11008 (16 x 43 full tiles, 2.69 rounds on 256
+// CUs) this gives 2 rounds of full tiles and 1 of narrow ones.
+constexpr double kNarrowCost = 0.8;
+static void large_split(int m_tiles, int strips, int* n_full, int* n_tail) {
+  const long cus = device_cus();
+  const int max_full = (strips + 15) / 16;
+  auto rounds = [&](long wgs) { return (wgs + cus - 1) / cus; };
+  auto tail_of = [&](int f) { return (std::max(0, strips - 16 * f) + 11) / 12; };
+  int best = max_full;
+  double best_cost = (double)rounds((long)m_tiles * max_full);
+  for (int f = max_full - 1; f >= 0; --f) {
+    const double c = rounds((long)m_tiles * f) + kNarrowCost * rounds((long)m_tiles * tail_of(f));
+    if (c < best_cost - 1e-9) {
+      best_cost = c;
+      best = f;
+    }
+  }
+  static const int want = env_int("QMM_LARGE_FULL_TILES");
+  if (want >= 0) best = std::min(want, max_full);
+  *n_full = best;
+  *n_tail = tail_of(best);
+}
+
 GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size, bool with_workspace) {
   GemmPlan p{};
   (void)group_size;
   static const int big = env_int("QMM_GEMM_LARGE_MIN_M");
   if (w_bit != 8 && M > (big > 0 ? big : 64) && K % 128 == 0) {
     p.kind = 1;
-    p.mtile = 16 * large_mt();
-    p.n_tiles = (N / 16 + 15) / 16;
+    p.mtile = 16 * kLargeMT;
     p.m_tiles = (M + p.mtile - 1) / p.mtile;
+    large_split(p.m_tiles, N / 16, &p.n_tiles, &p.tail_tiles);
     p.nt = 16;
     p.waves = 4;
     p.splits = 1;
@@ -990,18 +1181,21 @@ static hipError_t launch_gs(const MatmulArgs& a, const GemmPlan& p) {
   }
 }
 
-template <int W_BIT, int XDT, int GS, bool ZP, int MT>
-static hipError_t launch_large_mt(const MatmulArgs& a, const GemmPlan& p) {
-  return launch_kernel(gemm_large_kernel<W_BIT, XDT, GS, ZP, MT>,
-                       dim3((unsigned)(p.n_tiles * p.m_tiles)), dim3(256), a.stream, a.x, a.Q,
-                       a.scales, a.zeros, a.y, a.M, a.N, a.K,
-                       pack_tiles(p.n_tiles, a.y_dtype, a.group_mask == 0));
-}
-
 template <int W_BIT, int XDT, int GS, bool ZP>
 static hipError_t launch_large_k(const MatmulArgs& a, const GemmPlan& p) {
-  return p.mtile == 128 ? launch_large_mt<W_BIT, XDT, GS, ZP, 8>(a, p)
-                        : launch_large_mt<W_BIT, XDT, GS, ZP, 16>(a, p);
+  const bool per_column = a.group_mask == 0;
+  hipError_t e = hipSuccess;
+  if (p.n_tiles > 0)
+    e = launch_kernel(gemm_large_kernel<W_BIT, XDT, GS, ZP, 4>,
+                      dim3((unsigned)(p.n_tiles * p.m_tiles)), dim3(256), a.stream, a.x, a.Q,
+                      a.scales, a.zeros, a.y, a.M, a.N, a.K,
+                      pack_tiles(p.n_tiles, a.y_dtype, per_column), 0);
+  if (e == hipSuccess && p.tail_tiles > 0)
+    e = launch_kernel(gemm_large_kernel<W_BIT, XDT, GS, ZP, 3>,
+                      dim3((unsigned)(p.tail_tiles * p.m_tiles)), dim3(256), a.stream, a.x, a.Q,
+                      a.scales, a.zeros, a.y, a.M, a.N, a.K,
+                      pack_tiles(p.tail_tiles, a.y_dtype, per_column), 16 * p.n_tiles);
+  return e;
 }
 
 template <int W_BIT, int XDT, int GS>

@@ -294,12 +294,14 @@ static qmm_status gemm_impl(const char* fn, const void* x, const void* Q, const 
   // without a workspace the plan keeps every partial sum inside a workgroup
   const qmm::GemmPlan p = qmm::plan_gemm(M, N, K, w_bit, gs, noalloc || workspace != nullptr);
   if (p.kind < 0) return fail(QMM_ERR_UNSUPPORTED, "%s: no MFMA kernel for this shape", fn);
-  // the skinny kernels (and the tile GEMV) address a workgroup's x rows (up
-  // to 64 rows of K) and weight strips with 32-bit byte offsets
+  // the kernels address a workgroup's x rows (up to 64 rows of K; 256 for
+  // M > 64) and weight strips with 32-bit byte offsets
   if (p.kind != 1 && (int64_t)K * 128 >= (int64_t(1) << 31))
     return fail(QMM_ERR_UNSUPPORTED, "%s: K=%d too large for M <= 64 (K < 2^24)", fn, K);
+  if (p.kind == 1 && (int64_t)K * 512 >= (int64_t(1) << 31))
+    return fail(QMM_ERR_UNSUPPORTED, "%s: K=%d too large for M > 64 (K < 2^22)", fn, K);
   // ... and their scale and zero rows too: the scale table must stay below 2 GiB
-  if (p.kind != 1 && w_bit != 8) {
+  if (w_bit != 8) {
     const int64_t G = group_size == QMM_PER_COLUMN ? 1 : K / group_size;
     if (G * (int64_t)N >= (int64_t(1) << 30))
       return fail(QMM_ERR_UNSUPPORTED, "%s: scale table of %lld x %d too large (< 2^30 entries)",

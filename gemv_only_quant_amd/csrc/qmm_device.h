@@ -12,6 +12,7 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 enum { XF16 = 0, XBF16 = 1, YF32 = 2 };
 
@@ -105,9 +106,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
-// Work-item remap so that consecutive work ids land on one XCD: the
-// dispatcher deals workgroups round-robin over the 8 XCDs, so block b runs
-// on XCD b % 8.  Used only when the grid is a multiple of 8.
 // Raw buffer loads (no format conversion) through a descriptor whose range
 // is `bytes`: an offset at or past it reads zeros.  Word 3 is the raw-buffer
 // configuration of the CDNA buffer descriptor (32-bit data format, no
@@ -139,6 +137,9 @@ __device__ __forceinline__ u32x4_t buf_load128_coherent(buf_t b, int off) {
   return __builtin_amdgcn_raw_buffer_load_b128(b, off, 0, kCoherent);
 }
 
+// Work-item remap so that consecutive work ids land on one XCD: the
+// dispatcher deals workgroups round-robin over the 8 XCDs, so block b runs
+// on XCD b % 8.  Used only when the grid is a multiple of 8.
 __device__ __forceinline__ int xcd_remap(int b, int total) {
   if (total % 8 != 0) return b;
   return (b % 8) * (total / 8) + b / 8;

@@ -80,8 +80,9 @@ struct GemmPlan {
   int nt;        // 16-column strips per workgroup (skinny)
   int waves;     // waves per workgroup, splitting K (skinny: 4 or 8)
   int splits;    // workgroups per tile splitting K (skinny; 1 = none)
-  int n_tiles;
+  int n_tiles;   // column tiles (large-M: full 256-column tiles)
   int m_tiles;
+  int tail_tiles;  // large-M: narrow 192-column tiles after the full ones (0: none)
   size_t workspace_bytes;  // tickets + partial tiles when splits > 1, else 0
 };
 // with_workspace: whether the call has a workspace; without one the plan

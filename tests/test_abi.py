@@ -121,6 +121,10 @@ GEMM_BAD = [
     (dict(M=16, N=65536, K=524288, group_size=32), E_UNS, "too large"),
     # skinny kernel: 32-bit byte offsets into x (64 rows of K)
     (dict(M=16, N=64, K=1 << 24, group_size=128), E_UNS, "K=16777216 too large"),
+    # large-M kernel: 32-bit byte offsets into a workgroup's x rows (256 rows of K)
+    (dict(M=128, N=64, K=1 << 22, group_size=128), E_UNS, "K=4194304 too large for M > 64"),
+    # ... and into the scale table
+    (dict(M=128, N=65536, K=524288, group_size=32), E_UNS, "scale table"),
 ]
 
 

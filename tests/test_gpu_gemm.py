@@ -218,18 +218,43 @@ def test_gemm_large_within_bound(M, N, K, w_bit, gs, xdt, sym):
     assert_within_bound(y, y_ref, a_ref, f"gemm large w{w_bit} M{M} N{N} K{K}")
 
 
+# The large-M plan on 256 CUs: small grids run 192-column tiles only; these
+# shapes reach the 256-column kernel alone (one round of 16 x 16 tiles, where
+# narrow tiles would need two) and the split of full tiles followed by narrow
+# ones, with ragged rows and strips at the edges of each.
+LARGE_SPLIT = [  # M, N, K, w_bit, group, x_dtype, symmetric
+    (4000, 4048, 256, 4, 128, si.BF16, False),  # full tiles only; last M tile and wave ragged
+    (4096, 4096, 256, 2, 64, si.F16, False),    # full tiles only, int2
+    (3900, 6320, 256, 4, 64, si.F16, True),     # 16 full + 12 narrow column tiles, the last
+                                                # with 7 of its 12 strips inside N
+    (4096, 6400, 256, 2, 64, si.BF16, False),   # 16 full + 12 narrow column tiles, int2
+    (3900, 4416, 256, 4, 128, si.BF16, False),  # narrow tiles only (2 rounds of them beat
+                                                # 2 rounds of full ones)
+]
+
+
+@pytest.mark.parametrize("M,N,K,w_bit,gs,xdt,sym", LARGE_SPLIT)
+def test_gemm_large_full_and_narrow_tiles(M, N, K, w_bit, gs, xdt, sym):
+    case = si.lowbit_case(M, N, K, w_bit, gs, xdt, sym, seed=11 + M + N + K + w_bit)
+    y = run_gemm(case)
+    y_ref, a_ref = oracle.qmm_mt(*case.oracle_args())
+    assert_within_bound(y, y_ref, a_ref, f"gemm large split w{w_bit} M{M} N{N} K{K}")
+
+
 @pytest.mark.parametrize("M,N,K,w_bit,gs,xdt,sym", [
     (300, 48, 1024, 4, 128, si.BF16, False),
     (512, 1024, 1024, 4, 128, si.BF16, False),  # 8 tiles: the XCD-aware tile order
     (260, 32, 2048, 2, 64, si.F16, False),
     (128, 16, 512, 4, 32, si.BF16, True),
+    (3900, 6320, 256, 4, 128, si.F16, False),   # full then narrow column tiles
+    (4000, 4048, 256, 2, 64, si.BF16, False),   # full tiles only
 ])
 def test_gemm_large_exact_probe_bit_exact(M, N, K, w_bit, gs, xdt, sym):
     """Power-of-two scales keep (q - z) * s exact in 16 bits, so the
     pre-scaled operands and every summation order are exact."""
     case = si.exact_lowbit_case(M, N, K, w_bit, gs, xdt, sym, seed=M + K)
     y = run_gemm(case)
-    y_ref, _ = oracle.qmm(*case.oracle_args())
+    y_ref, _ = oracle.qmm_mt(*case.oracle_args())
     assert np.array_equal(y.astype(np.float64), y_ref)
 
 
