@@ -90,6 +90,13 @@ struct GemmPlan {
 GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size, bool with_workspace = true);
 hipError_t launch_gemm(const MatmulArgs& a, const GemmPlan& p);
 
+// ---- large-M MFMA GEMM (gemm_large.hip) ----------------------------------
+constexpr int kLargeRows = 256;  // rows per workgroup tile
+// Column split of a large-M plan: n_full 256-column tiles, then n_tail
+// 192-column ones, over `strips` 16-column strips and m_tiles row tiles.
+void large_split(int m_tiles, int strips, int* n_full, int* n_tail);
+hipError_t launch_gemm_large(const MatmulArgs& a, const GemmPlan& p);
+
 // ---- int8 x ternary (ternary.hip) -----------------------------------------
 hipError_t launch_t2_pack(const void* Wp, void* Wt, int N, int K, hipStream_t s);
 hipError_t launch_t2_unpack(const void* Wt, void* Wp, int N, int K, hipStream_t s);
