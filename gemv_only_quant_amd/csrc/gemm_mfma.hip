@@ -451,6 +451,36 @@ GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size, bool with_wor
     p.workspace_bytes = 0;
     return p;
   }
+  // int8 at 17-64 rows: the medium kernel, whose workgroups cover 128
+  // columns and share their x rows through LDS (the skinny kernel's 64-column
+  // workgroups each re-read all of x), K split over workgroups so that about
+  // one round of them covers the CUs.  It needs the split's workspace unless
+  // the tiles alone fill the CUs.
+  static const int want_med = env_int("QMM_MEDIUM");
+  static const int want_med_nt = env_int("QMM_MEDIUM_NT");
+  static const int want_med_s = env_int("QMM_MEDIUM_SPLITS");
+  if (w_bit == 8 && M > 16 && M <= 64 && K % 128 == 0 && want_med != 0) {
+    const int mmt = M <= 32 ? 2 : 4;
+    const int mnt = (want_med_nt == 2 || want_med_nt == 4) ? want_med_nt : 2;
+    const int n_tiles = (N / 16 + 4 * mnt - 1) / (4 * mnt);
+    const long tiles = n_tiles;
+    const int nst = K / 128;
+    int s = 1;
+    if (with_workspace)
+      while (s < 8 && tiles * (s + 1) <= 248 && nst / (s + 1) >= 4) ++s;
+    if (with_workspace && want_med_s >= 1 && want_med_s <= 16) s = want_med_s;
+    if (s > 1 || tiles >= 192) {
+      p.kind = 3;
+      p.mtile = 16 * mmt;
+      p.nt = mnt;
+      p.n_tiles = n_tiles;
+      p.m_tiles = 1;
+      p.waves = 4;
+      p.splits = s;
+      p.workspace_bytes = medium_workspace_bytes((int)tiles, s, mmt, mnt);
+      return p;
+    }
+  }
   int mt, nt;
   skinny_shape(M, N, &mt, &nt);
   p.kind = 0;
@@ -558,6 +588,7 @@ hipError_t launch_gemm(const MatmulArgs& a, const GemmPlan& p) {
   const bool f16 = a.x_dtype == XF16;
   if (p.kind == 2) return launch_gemv_tile(a);
   if (p.kind == 1) return launch_gemm_large(a, p);
+  if (p.kind == 3) return launch_gemm_medium(a, p);
   switch (a.w_bit) {
     case 4: return f16 ? launch_gs<4, XF16>(a, p) : launch_gs<4, XBF16>(a, p);
     case 2: return f16 ? launch_gs<2, XF16>(a, p) : launch_gs<2, XBF16>(a, p);

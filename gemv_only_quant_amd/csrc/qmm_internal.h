@@ -75,7 +75,8 @@ hipError_t launch_dequant(const void* Q, int layout, const void* scales, const v
 // ---- MFMA GEMM on the tile layout ---------------------------------------
 struct GemmPlan {
   int kind;      // 0: skinny (registers-direct, K split over the waves), 1: large-M tiled,
-                 // 2: VALU GEMV on the tile layout (small M, low-bit)
+                 // 2: VALU GEMV on the tile layout (small M, low-bit), 3: int8 medium M
+                 // (x shared through LDS, K split over workgroups)
   int mtile;     // rows per M tile
   int nt;        // 16-column strips per workgroup (skinny)
   int waves;     // waves per workgroup, splitting K (skinny: 4 or 8)
@@ -96,6 +97,12 @@ constexpr int kLargeRows = 256;  // rows per workgroup tile
 // 192-column ones, over `strips` 16-column strips and m_tiles row tiles.
 void large_split(int m_tiles, int strips, int* n_full, int* n_tail);
 hipError_t launch_gemm_large(const MatmulArgs& a, const GemmPlan& p);
+
+// ---- int8 MFMA GEMM at medium M (gemm_medium.hip) --------------------------
+// Workspace of a plan of `tiles` tiles split `splits` ways: tickets, then the
+// partial tiles (mt 16-row tiles x 4 nt strips per workgroup).
+size_t medium_workspace_bytes(int tiles, int splits, int mt, int nt);
+hipError_t launch_gemm_medium(const MatmulArgs& a, const GemmPlan& p);
 
 // ---- int8 x ternary (ternary.hip) -----------------------------------------
 hipError_t launch_t2_pack(const void* Wp, void* Wt, int N, int K, hipStream_t s);

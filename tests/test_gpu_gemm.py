@@ -65,6 +65,12 @@ INT8 = [  # M, N, K, x_dtype
     (33, 32, 320, si.BF16),
     (64, 112, 1024, si.F16),
     (70, 16, 128, si.BF16),
+    # 17-64 rows with K % 128 == 0 take the medium kernel: ragged rows, a
+    # last tile with 5 of its 8 strips, 9 stages split 5 + 4
+    (50, 592, 1152, si.BF16),
+    # 33 stages over 8 splits of 5: the last split has none (its workgroup
+    # adds an all-zero partial)
+    (20, 64, 4224, si.F16),
 ]
 
 
@@ -92,12 +98,26 @@ def test_gemm_lowbit_exact_probe_bit_exact(M, N, K, w_bit, gs, xdt, sym):
 @pytest.mark.parametrize("M,N,K,xdt", [(16, 32, 1024, si.BF16), (48, 16, 2048, si.F16),
                                         # odd count of 64-deep blocks: the last 128-deep
                                         # stage is half past K and its k steps are skipped
-                                        (16, 32, 192, si.BF16), (33, 48, 320, si.F16)])
+                                        (16, 32, 192, si.BF16), (33, 48, 320, si.F16),
+                                        # medium kernel: split 4 and 8 ways
+                                        (64, 112, 2048, si.BF16), (20, 64, 4224, si.F16)])
 def test_gemm_int8_exact_probe_bit_exact(M, N, K, xdt):
     case = si.exact_int8_case(M, N, K, xdt, seed=N + 1)
     y = run_gemm(case)
     y_ref, _ = oracle.qmm(*case.oracle_args())
     assert np.array_equal(y.astype(np.float64), y_ref)
+
+
+@pytest.mark.parametrize("ws", [None, NO_WORKSPACE])
+def test_gemm_int8_medium_unsplit(ws):
+    """192 column tiles of the medium kernel fill the CUs without a K split:
+    the same plan with and without a workspace."""
+    M, N, K = 40, 24576, 256
+    assert qmm.qmm_workspace_bytes(M, N, K, 8, 0) == 0
+    case = si.int8_case(M, N, K, si.BF16, seed=123)
+    y = run_gemm(case, ws=ws)
+    y_ref, a_ref = oracle.qmm_mt(*case.oracle_args())
+    assert_within_bound(y, y_ref, a_ref, "medium unsplit")
 
 
 def test_gemm_one_hot_reproduces_weights():

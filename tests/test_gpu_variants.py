@@ -94,7 +94,9 @@ OUT_CASES = [  # entry, M, N, K, w_bit, group, x_dtype
     ("gemv", 7, 64, 1024, 2, 64, si.BF16),
     ("gemv", 3, 48, 1024, 8, 0, si.BF16),          # int8 GEMV
     ("gemm", 16, 128, 2048, 4, 128, si.BF16),      # skinny
-    ("gemm", 32, 64, 1024, 8, 0, si.F16),          # skinny int8
+    ("gemm", 16, 64, 1024, 8, 0, si.F16),          # skinny int8
+    ("gemm", 32, 64, 1024, 8, 0, si.F16),          # medium int8, K split 2 ways
+    ("gemm", 64, 80, 2048, 8, 0, si.BF16),         # medium int8, 64 rows, ragged tile
     ("gemm", 130, 80, 1024, 4, 64, si.BF16),       # large-M kernel
     ("gemm", 100, 32, 512, 2, 32, si.F16),         # large-M kernel, int2
 ]
