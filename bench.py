@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--quick]
     python bench.py --probe WORKLOAD[@ENTRY]  (three calls, for rocprofv3 --pmc)
+    python bench.py --phases              (per-wave phase stamps of the headline GEMV)
     python bench.py --trace-summary DB    (per-workload rows of a rocprofv3 trace
                                            taken with --kernel-trace --marker-trace)
 
@@ -521,6 +522,87 @@ def trace_summary(db_path):
               f"{statistics.median(d):.3f} | {p90:.3f} | {d[0]:.3f} | {d[-1]:.3f} |")
 
 
+def phases(launches=200):
+    """Where the headline tile GEMV's time goes: per-wave real-time stamps
+    (100 MHz) from the stamp build of the library (gemv_only_quant_amd/
+    build.py --phases), beside the same stamps on a read-only kernel with
+    the same grid reading the same bytes per workgroup.  Each launch runs on
+    its own weight copy (a pool of >= 512 MB) after the previous one has
+    finished, and its stamps are read back before the next."""
+    import ctypes
+    import torch
+    import gemv_only_quant_amd as qmm
+    import synth_inputs as si
+
+    path = os.path.join(ROOT, "gemv_only_quant_amd", "libqmm_phases.so")
+    if not os.path.exists(path):
+        raise SystemExit(f"{path} is not built; run python gemv_only_quant_amd/build.py --phases")
+    lib = ctypes.CDLL(path)
+    vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.qmm_gemm.argtypes = [vp] * 5 + [ci] * 6 + [vp, sz, vp]
+    lib.qmm_gemm.restype = ci
+    lib.qmm_phase_stamps_read.argtypes = [vp, sz]
+    lib.qmm_phase_stamps_read.restype = ci
+    lib.qmm_phase_readonly.argtypes = [vp, vp, ci, ci, vp]
+    lib.qmm_phase_readonly.restype = ci
+
+    case = si.workload(HEADLINE)
+    d = case.to("cuda")
+    Q0 = qmm.pack(d.Q, case.N, case.K, case.w_bit)
+    wbytes = Q0.numel() * Q0.element_size()
+    copies = max(2, -(-POOL_BYTES // wbytes))
+    pool = [Q0] + [Q0.clone() for _ in range(copies - 1)]
+    y = torch.empty((case.M, case.N), dtype=torch.float32, device="cuda")
+    sink = torch.empty((case.N // 16) * 256, dtype=torch.int32, device="cuda")
+    waves = (case.N // 16) * 4
+    nblk = case.K // 128
+    stream = torch.cuda.current_stream().cuda_stream
+    buf = np.zeros(waves * 8, dtype=np.uint64)
+    x_dt = qmm.QMM_F16 if case.x_dtype == si.F16 else qmm.QMM_BF16
+
+    def gemv(i):
+        st = lib.qmm_gemm(d.x.data_ptr(), pool[i % copies].data_ptr(), d.scales.data_ptr(),
+                          d.zeros.data_ptr(), y.data_ptr(), case.M, case.N, case.K, case.w_bit,
+                          case.group_size, x_dt, None, 0, stream)
+        assert st == 0, st
+
+    def readonly(i):
+        assert lib.qmm_phase_readonly(pool[i % copies].data_ptr(), sink.data_ptr(),
+                                      case.N // 16, nblk, stream) == 0
+
+    def run(fn, slots):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        per_launch = []
+        for i in range(launches + 10):
+            ev0.record()
+            fn(i)
+            ev1.record()
+            torch.cuda.synchronize()
+            assert lib.qmm_phase_stamps_read(buf.ctypes.data, buf.size) == 0
+            if i < 10:
+                continue  # warm-up
+            t = buf.reshape(waves, 8).astype(np.int64)
+            t0 = t[:, 0]
+            row = {"event_us": ev0.elapsed_time(ev1) * 1e3,
+                   "span_us": (t[:, 5].max() - t0.min()) / 100.0,
+                   "entry_spread_us": (t0.max() - t0.min()) / 100.0,
+                   "wave_total_us": float(np.median(t[:, 5] - t0)) / 100.0}
+            for k, name in slots.items():
+                row[name] = float(np.median(t[:, k] - t0)) / 100.0
+            per_launch.append(row)
+        keys = per_launch[0].keys()
+        return {k: round(float(np.median([r[k] for r in per_launch])), 3) for k in keys}
+
+    g = run(gemv, {1: "x_slice_ready_us", 2: "group_table_ready_us", 3: "weights_consumed_us",
+                   4: "scales_in_lds_us"})
+    r = run(readonly, {3: "last_load_returned_us"})
+    # the same harness's graph-replayed time, for the launch floor
+    out = {"workload": HEADLINE, "launches": launches, "stamp_clock": "s_memrealtime, 100 MHz",
+           "tile_gemv": g, "read_only_same_grid": r}
+    print(json.dumps(out), flush=True)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -532,6 +614,8 @@ def main():
                     help="three calls of one workload and a 256 MiB copy, for counter runs")
     ap.add_argument("--trace-summary", metavar="DB",
                     help="per-workload kernel durations from a rocprofv3 trace database")
+    ap.add_argument("--phases", action="store_true",
+                    help="phase stamps of the headline GEMV (needs build.py --phases)")
     args = ap.parse_args()
     if args.trace_summary:
         trace_summary(args.trace_summary)
@@ -547,6 +631,9 @@ def main():
     torch.cuda.set_device(0)
     if args.probe:
         probe(args.probe)
+        return
+    if args.phases:
+        phases()
         return
     r = time_workload(HEADLINE, args.steps, args.warmup, HEADLINE_PATH)
     case, us = r["case"], r["us"]

@@ -34,12 +34,13 @@ def _stale(src, obj):
     return max(os.path.getmtime(d) for d in deps) > os.path.getmtime(obj)
 
 
-def _compile(src, verbose, incremental=False):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(src, verbose, incremental=False, defines=(), tag=""):
+    obj = os.path.join(BUILD, os.path.basename(src) + tag + ".o")
     if incremental and not _stale(src, obj):
         return obj
     lang = ["-x", "hip"]
-    cmd = [HIPCC] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + COMMON + [f"-D{d}" for d in defines] + lang + ["-c", os.path.join(CSRC, src),
+                                                                    "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -62,5 +63,26 @@ def build(verbose: bool = False, jobs: int = 8, incremental: bool = False) -> st
     return LIB
 
 
+PHASES_LIB = os.path.join(PKG, "libqmm_phases.so")
+
+
+def build_phases(verbose: bool = False) -> str:
+    """The phase-stamp library (measurement only, never loaded by the
+    package): the product objects, with the tile GEMV built with
+    QMM_PHASE_STAMPS (per-wave real-time stamps, a read-only reference
+    kernel).  Read by bench.py --phases."""
+    os.makedirs(BUILD, exist_ok=True)
+    objs = [_compile(s, verbose, incremental=True) for s in SOURCES if s != "gemv_tile.hip"]
+    objs.append(_compile("gemv_tile.hip", verbose, defines=("QMM_PHASE_STAMPS",), tag=".phases"))
+    tmp = PHASES_LIB + ".tmp"
+    subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs,
+                   check=True)
+    os.replace(tmp, PHASES_LIB)
+    return PHASES_LIB
+
+
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv, incremental="-i" in sys.argv)
+    if "--phases" in sys.argv:
+        build_phases(verbose="-v" in sys.argv)
+    else:
+        build(verbose="-v" in sys.argv, incremental="-i" in sys.argv)

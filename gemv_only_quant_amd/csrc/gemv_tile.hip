@@ -59,6 +59,28 @@ template <int W_BIT, int XDT> struct Pairs {
   static constexpr bool SPLIT = W_BIT == 4 && XDT == XF16;
 };
 
+// Phase stamps (QMM_PHASE_STAMPS builds only, never the product library):
+// lane 0 of every wave records the 100 MHz real-time counter at fixed
+// points of the kernel into a device array the host reads back.  Stamp
+// slots per wave: 0 entry, 1 x slice and its sums in LDS, 2 group-sum table
+// ready, 3 every weight block's dot products done (its loads returned),
+// 4 scales and zero words in LDS, 5 output stored.
+#ifdef QMM_PHASE_STAMPS
+constexpr int kStampSlots = 8;
+constexpr int kStampWaves = 4 * 8192;  // up to 8192 workgroups of 4 waves
+__device__ uint64_t phase_stamps[kStampWaves * kStampSlots];
+#define QMM_STAMP(slot)                                                              \
+  do {                                                                               \
+    const uint64_t t_ = __builtin_amdgcn_s_memrealtime();                            \
+    const int w_ = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);                     \
+    if ((threadIdx.x & 63) == 0 && w_ < kStampWaves) phase_stamps[w_ * kStampSlots + (slot)] = t_; \
+  } while (0)
+#else
+#define QMM_STAMP(slot) \
+  do {                  \
+  } while (0)
+#endif
+
 // m_ydt: M in bits 0-7, output type in bits 8-9; gs_opt: log2 of the group
 // size, or -1 for per-column scales (one group spanning K).  SPB: groups per
 // block, max(1, KB / group size) (1 for per-column scales).
@@ -88,6 +110,7 @@ __global__ __launch_bounds__(256) void gemv_tile_kernel(
   const int gmask = gs_opt < 0 ? 0 : -1;
   const int G = gs_opt < 0 ? 1 : K >> gsh;
 
+  QMM_STAMP(0);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, oct = lane >> 4;
@@ -186,6 +209,7 @@ __global__ __launch_bounds__(256) void gemv_tile_kernel(
       }
     }
     __syncthreads();
+    QMM_STAMP(1);
     // group sums of the pass: entry (m, block, e) adds the OPB / SPB octet
     // sums of group e of the block
 #pragma unroll
@@ -205,6 +229,7 @@ __global__ __launch_bounds__(256) void gemv_tile_kernel(
       }
     }
     __syncthreads();
+    QMM_STAMP(2);
 
     // 4. per block: dot products into per-block, per-group sums
     float bacc[NBW][MB][SPB];
@@ -261,6 +286,7 @@ __global__ __launch_bounds__(256) void gemv_tile_kernel(
           asm volatile("" : "+v"(bacc[i][m][e]));
         }
     }
+    QMM_STAMP(3);
 
     // 5. the pass's scales and zero words to LDS (the x slice and group table
     // are no longer written; every wave is past the table reads of step 3)
@@ -277,6 +303,7 @@ __global__ __launch_bounds__(256) void gemv_tile_kernel(
       if (u < ZR * 16) zl[u] = zu[j] | zfill;
     }
     __syncthreads();
+    QMM_STAMP(4);
 
     // 6. group epilogue: r += s (sum x (B + q) - B X - z X), where the
     // column-wide term (P + z X) is taken by the octet-0 lane alone (the
@@ -325,6 +352,7 @@ __global__ __launch_bounds__(256) void gemv_tile_kernel(
   };
   if constexpr (Y32) store(reinterpret_cast<float*>(y));
   else with_y(y, ydt, store);
+  QMM_STAMP(5);
 }
 
 // ---------------------------------------------------------------- host side
@@ -380,4 +408,49 @@ hipError_t launch_gemv_tile(const MatmulArgs& a) {
   return a.x_dtype == XF16 ? launch_tile_x<2, XF16>(a) : launch_tile_x<2, XBF16>(a);
 }
 
+#ifdef QMM_PHASE_STAMPS
+// The reference the stamps are read against: the same grid (one 256-thread
+// workgroup per 16-column strip), each workgroup reading its strip's
+// nblk KiB in 1 KiB wave loads, 8 per wave in flight, summing and storing
+// one value per lane.  Slots: 0 entry, 3 last load returned, 5 stored.
+__global__ __launch_bounds__(256) void phase_readonly_kernel(const u32x4_t* __restrict__ src,
+                                                             uint32_t* __restrict__ dst,
+                                                             int nblk) {
+  QMM_STAMP(0);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const buf_t b = make_buf(src + (size_t)blockIdx.x * nblk * 64, (uint32_t)nblk * 1024u);
+  uint32_t acc = 0;
+  for (int kb = wave * 8; kb < nblk; kb += 32) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = buf_load128(b, ((kb + i) * 64 + lane) * 16);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += v[i][0] ^ v[i][1] ^ v[i][2] ^ v[i][3];
+  }
+  asm volatile("" ::"v"(acc));  // every load has returned
+  QMM_STAMP(3);
+  dst[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
+  QMM_STAMP(5);
+}
+#endif
+
 }  // namespace qmm
+
+#ifdef QMM_PHASE_STAMPS
+// Host side of the stamp build: read the stamps back, and launch the
+// read-only reference on `strips` workgroups of nblk blocks each.
+extern "C" __attribute__((visibility("default"))) int qmm_phase_stamps_read(uint64_t* dst,
+                                                                            size_t count) {
+  if (count > (size_t)qmm::kStampWaves * qmm::kStampSlots) return -1;
+  return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(qmm::phase_stamps), count * sizeof(uint64_t), 0,
+                                  hipMemcpyDeviceToHost);
+}
+extern "C" __attribute__((visibility("default"))) int qmm_phase_readonly(const void* src,
+                                                                         void* dst, int strips,
+                                                                         int nblk, void* stream) {
+  if (strips <= 0 || strips > 8192 || nblk <= 0) return -1;
+  return (int)qmm::launch_kernel(qmm::phase_readonly_kernel, dim3((unsigned)strips), dim3(256),
+                                 reinterpret_cast<hipStream_t>(stream), src, dst, nblk);
+}
+#endif
