@@ -596,9 +596,34 @@ def phases(launches=200):
     g = run(gemv, {1: "x_slice_ready_us", 2: "group_table_ready_us", 3: "weights_consumed_us",
                    4: "scales_in_lds_us"})
     r = run(readonly, {3: "last_load_returned_us"})
+
+    # the matrix cores' sustained rate: 8 independent bf16 MFMAs per round on
+    # register operands, 4 workgroups per CU, zero and random operands
+    lib.qmm_calib_mfma.argtypes = [vp, vp, ci, ci, vp]
+    lib.qmm_calib_mfma.restype = ci
+    blocks, iters = 1024, 20000
+    sink2 = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    mfma = {}
+    gen = torch.Generator().manual_seed(5)
+    for label, seed in (("zero_operands", torch.zeros(128 * 8, dtype=torch.bfloat16)),
+                        ("random_operands", torch.randn(128 * 8, generator=gen).to(torch.bfloat16))):
+        sd = seed.to("cuda")
+        assert lib.qmm_calib_mfma(sd.data_ptr(), sink2.data_ptr(), blocks, 100, stream) == 0
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        assert lib.qmm_calib_mfma(sd.data_ptr(), sink2.data_ptr(), blocks, iters, stream) == 0
+        ev1.record()
+        torch.cuda.synchronize()
+        secs = ev0.elapsed_time(ev1) * 1e-3
+        flops = blocks * 4 * iters * 8 * 2.0 * 16 * 16 * 32
+        mfma[label] = {"ms": round(secs * 1e3, 3), "tflops": round(flops / secs / 1e12, 1),
+                       "frac_of_2500": round(flops / secs / 1e12 / MFMA_PEAK_TFLOPS, 4)}
     # the same harness's graph-replayed time, for the launch floor
     out = {"workload": HEADLINE, "launches": launches, "stamp_clock": "s_memrealtime, 100 MHz",
-           "tile_gemv": g, "read_only_same_grid": r}
+           "tile_gemv": g, "read_only_same_grid": r,
+           "mfma_loop_bf16_16x16x32": dict(mfma, blocks=blocks, waves_per_block=4,
+                                           rounds=iters, mfma_per_round=8)}
     print(json.dumps(out), flush=True)
     return out
 

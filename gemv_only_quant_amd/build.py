@@ -70,10 +70,12 @@ def build_phases(verbose: bool = False) -> str:
     """The phase-stamp library (measurement only, never loaded by the
     package): the product objects, with the tile GEMV built with
     QMM_PHASE_STAMPS (per-wave real-time stamps, a read-only reference
-    kernel).  Read by bench.py --phases."""
+    kernel), plus calibrate.hip (a register-only MFMA loop).  Read by
+    bench.py --phases."""
     os.makedirs(BUILD, exist_ok=True)
     objs = [_compile(s, verbose, incremental=True) for s in SOURCES if s != "gemv_tile.hip"]
     objs.append(_compile("gemv_tile.hip", verbose, defines=("QMM_PHASE_STAMPS",), tag=".phases"))
+    objs.append(_compile("calibrate.hip", verbose))
     tmp = PHASES_LIB + ".tmp"
     subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs,
                    check=True)
