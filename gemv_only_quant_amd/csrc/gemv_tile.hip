@@ -72,7 +72,7 @@ __device__ uint64_t phase_stamps[kStampWaves * kStampSlots];
 #define QMM_STAMP(slot)                                                              \
   do {                                                                               \
     const uint64_t t_ = __builtin_amdgcn_s_memrealtime();                            \
-    const int w_ = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);                     \
+    const int w_ = (int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6));       \
     if ((threadIdx.x & 63) == 0 && w_ < kStampWaves) phase_stamps[w_ * kStampSlots + (slot)] = t_; \
   } while (0)
 #else
@@ -84,13 +84,14 @@ __device__ uint64_t phase_stamps[kStampWaves * kStampSlots];
 // m_ydt: M in bits 0-7, output type in bits 8-9; gs_opt: log2 of the group
 // size, or -1 for per-column scales (one group spanning K).  SPB: groups per
 // block, max(1, KB / group size) (1 for per-column scales).
-template <int W_BIT, int XDT, int MB, int NBW, int SPB, bool Y32>
-__global__ __launch_bounds__(256) void gemv_tile_kernel(
+template <int W_BIT, int XDT, int MB, int NBW, int SPB, bool Y32, int WV>
+__global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ Qt,
     const uint16_t* __restrict__ sc, const uint32_t* __restrict__ qz, void* __restrict__ y,
     int m_ydt, int N, int K, int gs_opt) {
   constexpr int KB = TileK<W_BIT>::KB, PACK = TileK<W_BIT>::PACK;
-  constexpr int PASS_K = 4 * NBW * KB;           // k per pass
+  constexpr int NTH = 64 * WV;                   // threads per workgroup
+  constexpr int PASS_K = WV * NBW * KB;          // k per pass
   constexpr int PO = PASS_K / 8;                 // 8-k octets per pass
   constexpr int OPB = KB / 8;                    // octets per block
   constexpr int UPB = KB / 32;                   // 32-k units per block (per lane: one octet each)
@@ -98,8 +99,8 @@ __global__ __launch_bounds__(256) void gemv_tile_kernel(
   constexpr uint32_t ZMASK = (1u << W_BIT) - 1u;
   constexpr bool SPLIT = Pairs<W_BIT, XDT>::SPLIT;
   constexpr int NS = SPLIT ? 2 : 1;              // sums per octet / accumulators per group
-  constexpr int GPP = 4 * NBW * SPB;             // groups per pass at most
-  constexpr int TE = MB * 4 * NBW * SPB;         // group-sum entries per pass
+  constexpr int GPP = WV * NBW * SPB;            // groups per pass at most
+  constexpr int TE = MB * WV * NBW * SPB;        // group-sum entries per pass
   constexpr int ZR = GPP / PACK + 2;             // zero rows per pass at most
   constexpr float B = Bias<XDT>::value;
   const int M = m_ydt & 0xFF;
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(256) void gemv_tile_kernel(
   __shared__ __attribute__((aligned(16))) float2 gtab[2][TE];
   __shared__ uint16_t sl[GPP * 16];
   __shared__ uint32_t zl[ZR * 16];
-  __shared__ float red[4][MB][16];
+  __shared__ float red[WV][MB][16];
 
   // descriptors: a block past the strip, a row past M, a group past G read 0
   const buf_t qbuf = make_buf(Qt + (size_t)s * nblk * 64, (uint32_t)nblk * 1024u);
@@ -151,9 +152,9 @@ __global__ __launch_bounds__(256) void gemv_tile_kernel(
   asm("v_mov_b32 %0, %1" : "=v"(mhi) : "i"(FIELD2 << 4));
 
   constexpr int XCH = MB * PO;                   // 16-byte x chunks (one octet each)
-  constexpr int XPT = (XCH + 255) / 256;
-  constexpr int SU = (GPP * 8 + 255) / 256;      // 4-byte scale units (2 columns) per thread
-  constexpr int ZU = (ZR * 16 + 255) / 256;      // zero words per thread
+  constexpr int XPT = (XCH + NTH - 1) / NTH;
+  constexpr int SU = (GPP * 8 + NTH - 1) / NTH;  // 4-byte scale units (2 columns) per thread
+  constexpr int ZU = (ZR * 16 + NTH - 1) / NTH;  // zero words per thread
   for (int k0 = 0; k0 < K; k0 += PASS_K) {
     const int gp0 = (k0 >> gsh) & gmask;         // first group of the pass
     const int zr0 = gp0 / PACK;                  // first zero row of the pass
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(256) void gemv_tile_kernel(
     u32x4_t xr[XPT];
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
-      const int q = threadIdx.x + 256 * j;
+      const int q = threadIdx.x + NTH * j;
       const int m = q / PO, k = k0 + 8 * (q % PO);
       xr[j] = buf_load128(xbuf, (q < XCH && m < M && k < K) ? (m * K + k) * 2 : OUT);
     }
@@ -176,21 +177,21 @@ __global__ __launch_bounds__(256) void gemv_tile_kernel(
     uint32_t su[SU], zu[ZU];
 #pragma unroll
     for (int j = 0; j < SU; ++j) {
-      const int u = threadIdx.x + 256 * j;
+      const int u = threadIdx.x + NTH * j;
       const int gl = u >> 3, cp = u & 7;
       su[j] = buf_load32(sbuf, u < GPP * 8 ? ((gp0 + gl) * N + 2 * cp) * 2 : OUT);
     }
 #pragma unroll
     for (int j = 0; j < ZU; ++j) {
-      const int u = threadIdx.x + 256 * j;
+      const int u = threadIdx.x + NTH * j;
       zu[j] = buf_load32(zbuf, u < ZR * 16 ? ((zr0 + (u >> 4)) * N + (u & 15)) * 4 : OUT);
     }
     // 3. the pass to LDS
     if (k0 > 0) __syncthreads();  // the previous pass is done reading
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
-      const int q = threadIdx.x + 256 * j;
-      if (XCH % 256 == 0 || q < XCH) {
+      const int q = threadIdx.x + NTH * j;
+      if (XCH % NTH == 0 || q < XCH) {
         *reinterpret_cast<u32x4_t*>(xl + 8 * q) = xr[j];
         const int dst = q;  // (row, octet) in slice order
         if constexpr (SPLIT) {
@@ -213,10 +214,10 @@ __global__ __launch_bounds__(256) void gemv_tile_kernel(
     // group sums of the pass: entry (m, block, e) adds the OPB / SPB octet
     // sums of group e of the block
 #pragma unroll
-    for (int j = 0; j < (TE + 255) / 256; ++j) {
-      const int u = threadIdx.x + 256 * j;
-      if (TE % 256 == 0 || u < TE) {
-        const int m = u / (4 * NBW * SPB), be = u % (4 * NBW * SPB);
+    for (int j = 0; j < (TE + NTH - 1) / NTH; ++j) {
+      const int u = threadIdx.x + NTH * j;
+      if (TE % NTH == 0 || u < TE) {
+        const int m = u / (WV * NBW * SPB), be = u % (WV * NBW * SPB);
         const float* o = xsum + NS * (m * PO + be * (OPB / SPB));
         float xu = 0.f, x16 = 0.f;
 #pragma unroll
@@ -292,14 +293,14 @@ __global__ __launch_bounds__(256) void gemv_tile_kernel(
     // are no longer written; every wave is past the table reads of step 3)
 #pragma unroll
     for (int j = 0; j < SU; ++j) {
-      const int u = threadIdx.x + 256 * j;
+      const int u = threadIdx.x + NTH * j;
       if (u < GPP * 8) reinterpret_cast<uint32_t*>(sl)[u] = su[j];
     }
     // symmetric: every zero field holds 2^(w_bit-1) (the descriptor read 0)
     const uint32_t zfill = zp ? 0u : (W_BIT == 4 ? 0x88888888u : 0xAAAAAAAAu);
 #pragma unroll
     for (int j = 0; j < ZU; ++j) {
-      const int u = threadIdx.x + 256 * j;
+      const int u = threadIdx.x + NTH * j;
       if (u < ZR * 16) zl[u] = zu[j] | zfill;
     }
     __syncthreads();
@@ -320,7 +321,7 @@ __global__ __launch_bounds__(256) void gemv_tile_kernel(
         const float zf = (float)((zl[(g / PACK - zr0) * 16 + col] >> ((g % PACK) * W_BIT)) & ZMASK);
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
-          const float2 pe = gtab[oct != 0][(m * 4 * NBW + (kb - k0 / KB)) * SPB + e];
+          const float2 pe = gtab[oct != 0][(m * WV * NBW + (kb - k0 / KB)) * SPB + e];
           r[m] += sv * (bacc[i][m][e] - (pe.x + zf * pe.y));
         }
       }
@@ -345,7 +346,9 @@ __global__ __launch_bounds__(256) void gemv_tile_kernel(
     if (threadIdx.x < 16 * MB) {
       const int m = threadIdx.x >> 4, c = threadIdx.x & 15;
       if (m < M) {
-        const float sum = red[0][m][c] + red[1][m][c] + red[2][m][c] + red[3][m][c];
+        float sum = red[0][m][c];
+#pragma unroll
+        for (int v = 1; v < WV; ++v) sum += red[v][m][c];
         yt[(size_t)m * N + 16 * s + c] = (T)sum;
       }
     }
@@ -360,24 +363,27 @@ __global__ __launch_bounds__(256) void gemv_tile_kernel(
 // should have blocks inside K -- int2 (256-deep blocks) takes 4, a pass of
 // 4096 k; int4 takes 8 (4096 k) when K has at least 32 blocks, else 4.  The
 // x slice of 4 rows is then at most 32 KiB of LDS.
-template <int W_BIT, int XDT, int MB, int SPB, int NBW>
+template <int W_BIT, int XDT, int MB, int SPB, int NBW, int WV>
 static hipError_t launch_tile_nbw(const MatmulArgs& a) {
   const int gs_opt = a.group_mask == 0 ? -1 : __builtin_ctz((unsigned)a.group_size);
   const int m_ydt = a.M | ((a.y_dtype == YF32 ? 0 : a.y_dtype) << 8);
-  const dim3 grid((unsigned)(a.N / 16)), block(256);
+  const dim3 grid((unsigned)(a.N / 16)), block(64 * WV);
   if (a.y_dtype == YF32)
-    return launch_kernel(gemv_tile_kernel<W_BIT, XDT, MB, NBW, SPB, true>, grid, block, a.stream,
-                         a.x, a.Q, a.scales, a.zeros, a.y, m_ydt, a.N, a.K, gs_opt);
-  return launch_kernel(gemv_tile_kernel<W_BIT, XDT, MB, NBW, SPB, false>, grid, block, a.stream,
-                       a.x, a.Q, a.scales, a.zeros, a.y, m_ydt, a.N, a.K, gs_opt);
+    return launch_kernel(gemv_tile_kernel<W_BIT, XDT, MB, NBW, SPB, true, WV>, grid, block,
+                         a.stream, a.x, a.Q, a.scales, a.zeros, a.y, m_ydt, a.N, a.K, gs_opt);
+  return launch_kernel(gemv_tile_kernel<W_BIT, XDT, MB, NBW, SPB, false, WV>, grid, block,
+                       a.stream, a.x, a.Q, a.scales, a.zeros, a.y, m_ydt, a.N, a.K, gs_opt);
 }
 
 template <int W_BIT, int XDT, int MB, int SPB>
 static hipError_t launch_tile_spb(const MatmulArgs& a) {
   if constexpr (W_BIT == 4) {
-    if (a.K / TileK<4>::KB >= 32) return launch_tile_nbw<W_BIT, XDT, MB, SPB, 8>(a);
+    // 4 waves of 8 blocks per pass: measured at M=1 K=N=4096 int4 g128
+    // against 2 waves of 16 blocks (5.63 us) and 8 waves of 4 (5.07 us):
+    // 4.84 us on the same box
+    if (a.K / TileK<4>::KB >= 32) return launch_tile_nbw<W_BIT, XDT, MB, SPB, 8, 4>(a);
   }
-  return launch_tile_nbw<W_BIT, XDT, MB, SPB, 4>(a);
+  return launch_tile_nbw<W_BIT, XDT, MB, SPB, 4, 4>(a);
 }
 
 template <int W_BIT, int XDT, int MB>
