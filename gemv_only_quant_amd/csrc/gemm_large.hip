@@ -224,12 +224,17 @@ __device__ __forceinline__ uint32_t mfma_row_deq_f16(f32x4_t (&c)[3], const u32x
   return out;
 }
 
+// x tile of a stage in LDS: MT row tiles x 4 k steps of 1 KiB fragments
+constexpr int kLargeFrags = kLargeMT * 4;
+
+// One workgroup's tile: work item `bid` of `nblocks` over n_tiles column
+// tiles of 16 NT columns starting at strip strip0, and every M tile.
 template <int W_BIT, int XDT, int GS, bool ZP, int NT>
-__global__ __launch_bounds__(256, 1) void gemm_large_kernel(
+__device__ __forceinline__ void large_body(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ Qt,
     const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qz, void* __restrict__ y,
-    int M, int N, int K, int tile_opts, int strip0) {
-  const int n_tiles = tiles_of(tile_opts), ydt = ydt_of(tile_opts), gmask = gmask_of(tile_opts);
+    int M, int N, int K, int n_tiles, int ydt, int gmask, int strip0, int bid, int nblocks,
+    u32x4_t (*xa)[kLargeFrags * 64]) {
   constexpr int MT = kLargeMT;          // 16-row tiles per workgroup
   constexpr int BM = 16 * MT;           // rows per workgroup
   constexpr int KS = 128;               // k per stage
@@ -241,7 +246,7 @@ __global__ __launch_bounds__(256, 1) void gemm_large_kernel(
   // symmetric zero 2^(w_bit-1) in every field of a word
   constexpr uint32_t ZSYM = W_BIT == 4 ? 0x88888888u : 0xAAAAAAAAu;
 
-  __shared__ u32x4_t xa[2][FRAGS * 64];
+  static_assert(FRAGS == kLargeFrags, "LDS tile");
 
   // fp16 1024 in both halves, held in a register: mask-and-or of the codes
   // is then one v_and_or_b32 (an instruction takes one literal at most)
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(256, 1) void gemm_large_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, quad = lane >> 4;
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int w = xcd_remap(bid, nblocks);
   const int nt = w % n_tiles, mt_idx = w / n_tiles;
   const int m0 = mt_idx * BM;
   const int strips = N / 16;
@@ -559,6 +564,30 @@ __global__ __launch_bounds__(256, 1) void gemm_large_kernel(
   });
 }
 
+
+// The whole plan in one launch: work items [0, full) take full tiles (4
+// strips per wave) over the first n_full column tiles, the rest narrow tiles
+// (3 strips per wave) over the remaining columns.  Workgroups are dispatched
+// in order, so the narrow ones start on whichever CUs free up first.  The
+// branch is uniform per workgroup; both bodies share the one LDS tile.
+template <int W_BIT, int XDT, int GS, bool ZP>
+__global__ __launch_bounds__(256, 1) void gemm_large_kernel(
+    const uint16_t* __restrict__ x, const u32x4_t* __restrict__ Qt,
+    const uint16_t* __restrict__ scales, const uint32_t* __restrict__ qz, void* __restrict__ y,
+    int M, int N, int K, int tile_opts, int tail_tiles) {
+  __shared__ u32x4_t xa[2][kLargeFrags * 64];
+  const int n_full = tiles_of(tile_opts), ydt = ydt_of(tile_opts), gmask = gmask_of(tile_opts);
+  const int m_tiles = (M + kLargeRows - 1) / kLargeRows;
+  const int full = n_full * m_tiles;
+  const int b = (int)blockIdx.x;
+  if (b < full)
+    large_body<W_BIT, XDT, GS, ZP, 4>(x, Qt, scales, qz, y, M, N, K, n_full, ydt, gmask, 0, b,
+                                      full, xa);
+  else
+    large_body<W_BIT, XDT, GS, ZP, 3>(x, Qt, scales, qz, y, M, N, K, tail_tiles, ydt, gmask,
+                                      16 * n_full, b - full, (int)gridDim.x - full, xa);
+}
+
 // ---------------------------------------------------------------- host side
 // Compute units of the current device (256 on MI355X), read once per device.
 static int device_cus() {
@@ -607,19 +636,10 @@ void large_split(int m_tiles, int strips, int* n_full, int* n_tail) {
 
 template <int W_BIT, int XDT, int GS, bool ZP>
 static hipError_t launch_large_k(const MatmulArgs& a, const GemmPlan& p) {
-  const bool per_column = a.group_mask == 0;
-  hipError_t e = hipSuccess;
-  if (p.n_tiles > 0)
-    e = launch_kernel(gemm_large_kernel<W_BIT, XDT, GS, ZP, 4>,
-                      dim3((unsigned)(p.n_tiles * p.m_tiles)), dim3(256), a.stream, a.x, a.Q,
-                      a.scales, a.zeros, a.y, a.M, a.N, a.K,
-                      pack_tiles(p.n_tiles, a.y_dtype, per_column), 0);
-  if (e == hipSuccess && p.tail_tiles > 0)
-    e = launch_kernel(gemm_large_kernel<W_BIT, XDT, GS, ZP, 3>,
-                      dim3((unsigned)(p.tail_tiles * p.m_tiles)), dim3(256), a.stream, a.x, a.Q,
-                      a.scales, a.zeros, a.y, a.M, a.N, a.K,
-                      pack_tiles(p.tail_tiles, a.y_dtype, per_column), 16 * p.n_tiles);
-  return e;
+  return launch_kernel(gemm_large_kernel<W_BIT, XDT, GS, ZP>,
+                       dim3((unsigned)((p.n_tiles + p.tail_tiles) * p.m_tiles)), dim3(256),
+                       a.stream, a.x, a.Q, a.scales, a.zeros, a.y, a.M, a.N, a.K,
+                       pack_tiles(p.n_tiles, a.y_dtype, a.group_mask == 0), p.tail_tiles);
 }
 
 template <int W_BIT, int XDT, int GS>
