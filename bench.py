@@ -593,8 +593,8 @@ def phases(launches=200):
         keys = per_launch[0].keys()
         return {k: round(float(np.median([r[k] for r in per_launch])), 3) for k in keys}
 
-    g = run(gemv, {1: "x_slice_ready_us", 2: "group_table_ready_us", 3: "weights_consumed_us",
-                   4: "scales_in_lds_us"})
+    g = run(gemv, {1: "x_slice_ready_us", 2: "group_table_ready_us", 6: "first_block_done_us",
+                   7: "half_blocks_done_us", 3: "weights_consumed_us", 4: "scales_in_lds_us"})
     r = run(readonly, {3: "last_load_returned_us"})
 
     # the matrix cores' sustained rate: 8 independent bf16 MFMAs per round on

@@ -64,7 +64,8 @@ template <int W_BIT, int XDT> struct Pairs {
 // points of the kernel into a device array the host reads back.  Stamp
 // slots per wave: 0 entry, 1 x slice and its sums in LDS, 2 group-sum table
 // ready, 3 every weight block's dot products done (its loads returned),
-// 4 scales and zero words in LDS, 5 output stored.
+// 4 scales and zero words in LDS, 5 output stored, 6 the first block's dot
+// products done, 7 the first half of the blocks' done.
 #ifdef QMM_PHASE_STAMPS
 constexpr int kStampSlots = 8;
 constexpr int kStampWaves = 4 * 8192;  // up to 8192 workgroups of 4 waves
@@ -232,12 +233,29 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
     __syncthreads();
     QMM_STAMP(2);
 
-    // 4. per block: dot products into per-block, per-group sums
+    // 4. per block: dot products into per-block, per-group sums.  The x
+    // operands of block i + 1 are read from LDS while block i is multiplied
+    // (when they fit in 32 registers): read just before their use, the LDS
+    // latency stood between every two words' dot products.
     float bacc[NBW][MB][SPB];
+    constexpr bool XPF = MB * UPB * 4 <= 32;
+    u32x4_t xc[XPF ? MB : 1][XPF ? UPB : 1], xn[XPF ? MB : 1][XPF ? UPB : 1];
+    auto read_x = [&](int i, u32x4_t (&dst)[XPF ? MB : 1][XPF ? UPB : 1]) {
+      const int kl = (kb0 + i) * KB - k0;
+#pragma unroll
+      for (int m = 0; m < (XPF ? MB : 1); ++m)
+#pragma unroll
+        for (int un = 0; un < (XPF ? UPB : 1); ++un)
+          dst[m][un] = *reinterpret_cast<const u32x4_t*>(xl + m * PASS_K + kl + 32 * un + 8 * oct);
+    };
+    if constexpr (XPF) read_x(0, xc);
 #pragma unroll
     for (int i = 0; i < NBW; ++i) {
       const int kb = kb0 + i;
       const int kl = kb * KB - k0;               // block start within the pass
+      if constexpr (XPF) {
+        if (i + 1 < NBW) read_x(i + 1, xn);
+      }
       float acc[MB][SPB][NS];
 #pragma unroll
       for (int m = 0; m < MB; ++m)
@@ -268,8 +286,9 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
           // rows past M hold zeros in xl and add nothing
 #pragma unroll
           for (int m = 0; m < MB; ++m) {
-            const u32x4_t xv =
-                *reinterpret_cast<const u32x4_t*>(xl + m * PASS_K + kl + 32 * un + 8 * oct);
+            u32x4_t xv;
+            if constexpr (XPF) xv = xc[m][un];
+            else xv = *reinterpret_cast<const u32x4_t*>(xl + m * PASS_K + kl + 32 * un + 8 * oct);
 #pragma unroll
             for (int t = 0; t < 4; ++t)
               acc[m][e][SPLIT ? (t & 1) : 0] =
@@ -286,6 +305,16 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
           // the scale loads (else they would be sunk to the epilogue)
           asm volatile("" : "+v"(bacc[i][m][e]));
         }
+      if constexpr (XPF) {
+        if (i + 1 < NBW) {
+#pragma unroll
+          for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int un = 0; un < UPB; ++un) xc[m][un] = xn[m][un];
+        }
+      }
+      if (i == 0) QMM_STAMP(6);
+      if (i == NBW / 2 - 1) QMM_STAMP(7);
     }
     QMM_STAMP(3);
 
