@@ -5,21 +5,23 @@
 // The skinny kernel (gemm_mfma.hip) gives each workgroup 64 columns, so at
 // 64 rows every workgroup reads all of x (64 x K) for 64 columns of
 // weights: at N = 14336 the 224 workgroups fetch x 224 times, twice the
-// weights' bytes.  Here a workgroup covers 16 NT columns (4 waves side by
-// side along N, NT strips each) and shares one copy of its x rows through
-// LDS, as the large-M kernel does; to keep every CU busy, K is split over S
-// workgroups per tile, each writing its partial tile to the workspace, and
-// the last of a tile's S workgroups to arrive adds them in split order.
-//  * x: 16 MT rows x 128 k per stage, buffer loads straight to LDS in the
-//    swizzled row layout (chunk c of row r at slot 16 r + (c ^ r)),
-//    double-buffered; every A operand is one conflict-free ds_read_b128;
+// weights' bytes.  Here a workgroup covers 128 columns (WV waves side by
+// side along N, NT strips each: 4 x 2 at 32 rows, 8 x 1 at 64) and shares
+// one copy of its x rows through LDS, as the large-M kernel does; to keep
+// every CU busy, K is split over S workgroups per tile, each writing its
+// partial tile to the workspace, and the last of a tile's S workgroups to
+// arrive adds them in split order.
+//  * x: 16 MT rows x 128 k per stage, buffer loads into the stage's ring
+//    registers, written at the top of the stage to a double-buffered LDS
+//    tile in the swizzled row layout (chunk c of row r at slot 16 r +
+//    (c ^ r)); every A operand is one conflict-free ds_read_b128;
 //  * weights: each wave streams its strips' 1 KiB blocks from the tile
-//    layout straight into B operands, two stages ahead; the int8 codes
+//    layout straight into B operands, a 4-deep ring of stages; the int8 codes
 //    become exact 16-bit floats (fp16: the code's byte under the 1024
 //    exponent, minus 1152; bf16: a signed byte convert) and the matrix
 //    cores form x . q exactly per product, summed in fp32;
 //  * partial tiles go out with coherent (L2-bypassing) stores in the
-//    accumulator layout, whole 4 KiB runs per instruction; one agent-scope
+//    accumulator layout, whole 1 KiB runs per wave instruction; one agent-scope
 //    ticket per tile elects the last workgroup, which re-arms it.
 #include <type_traits>
 
@@ -75,8 +77,8 @@ template <> __device__ __forceinline__ u32x4_t i8_operand<XBF16>(uint32_t lo, ui
 
 }  // namespace
 
-template <int XDT, int MT, int NT, int D, bool SPLIT>
-__global__ __launch_bounds__(256, 1) void gemm_int8_medium_kernel(
+template <int XDT, int MT, int NT, int WV, int D, bool SPLIT>
+__global__ __launch_bounds__(64 * WV, 1) void gemm_int8_medium_kernel(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ Qt,
     const float* __restrict__ scales, void* __restrict__ y, uint32_t* __restrict__ ws, int M,
     int N, int K, int tile_opts) {
@@ -86,7 +88,7 @@ __global__ __launch_bounds__(256, 1) void gemm_int8_medium_kernel(
   constexpr int STEPS = KS / 32;        // MFMA k steps per stage
   constexpr int FRAGS = MT * STEPS;     // 1 KiB x units per stage
   constexpr int BM = 16 * MT;
-  static_assert(FRAGS % 4 == 0, "whole load units per wave");
+  static_assert(FRAGS % WV == 0, "whole load units per wave");
 
   __shared__ u32x4_t xa[2][FRAGS * 64];
 
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(256, 1) void gemm_int8_medium_kernel(
   const int nt = w % n_tiles, mt_idx = w / n_tiles;
   const int m0 = mt_idx * BM;
   const int strips = N / 16;
-  const int s0 = (nt * 4 + wave) * NT;  // this wave's first strip
+  const int s0 = (nt * WV + wave) * NT;  // this wave's first strip
   const int nblk = K / KB;
   // this workgroup's stages of K
   const int nst_all = K / KS;
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(256, 1) void gemm_int8_medium_kernel(
   // slot count only the later slots' loads (a load straight to LDS in
   // flight makes it wait for every load).
   auto x_unit = [&](int j, int st) {
-    const int f = wave * (FRAGS / 4) + j;
+    const int f = wave * (FRAGS / WV) + j;
     const int c = f % 4;
     const int r = 4 * c + quad;
     return __builtin_amdgcn_raw_buffer_load_b128(
@@ -131,7 +133,7 @@ __global__ __launch_bounds__(256, 1) void gemm_int8_medium_kernel(
   };
   struct WRegs {
     u32x4_t slot[NT][2];
-    u32x4_t xr[FRAGS / 4];
+    u32x4_t xr[FRAGS / WV];
   };
   auto load_slot = [&](int s, int b, int st, WRegs& R) {
     R.slot[s][b] = __builtin_amdgcn_raw_buffer_load_b128(
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(256, 1) void gemm_int8_medium_kernel(
   WRegs ring[D];
   auto issue = [&](int t, int d) {
 #pragma unroll
-    for (int j = 0; j < FRAGS / 4; ++j) ring[d].xr[j] = x_unit(j, t);
+    for (int j = 0; j < FRAGS / WV; ++j) ring[d].xr[j] = x_unit(j, t);
     load_w(t, ring[d]);
   };
   if (nst > 0) {
@@ -175,8 +177,8 @@ __global__ __launch_bounds__(256, 1) void gemm_int8_medium_kernel(
         __builtin_amdgcn_sched_barrier(0);
         u32x4_t* xs_buf = &xa[t & 1][0];
 #pragma unroll
-        for (int j = 0; j < FRAGS / 4; ++j)
-          xs_buf[(wave * (FRAGS / 4) + j) * 64 + lane] = ring[d].xr[j];
+        for (int j = 0; j < FRAGS / WV; ++j)
+          xs_buf[(wave * (FRAGS / WV) + j) * 64 + lane] = ring[d].xr[j];
         __syncthreads();
         const WRegs& cur = ring[d];
 #pragma unroll
@@ -234,7 +236,8 @@ __global__ __launch_bounds__(256, 1) void gemm_int8_medium_kernel(
     // with coherent loads, in split order.  Nobody waits on anybody.
     const int tiles = gridDim.x / S;
     uint32_t* tickets = ws;
-    constexpr int PART = MT * NT * 256;  // 16-byte units per partial
+    constexpr int NTH = 64 * WV;
+    constexpr int PART = MT * NT * NTH;  // 16-byte units per partial
     const buf_t pbuf = make_buf(ws + ((tiles + 63) & ~63) + (size_t)w * S * PART * 4,
                                 (uint32_t)(S * PART * 16));
 #pragma unroll
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(256, 1) void gemm_int8_medium_kernel(
 #pragma unroll
       for (int s = 0; s < NT; ++s)
         buf_store128_coherent(__builtin_bit_cast(u32x4_t, acc[i][s]), pbuf,
-                              ((split * MT * NT + i * NT + s) * 256 + (int)threadIdx.x) * 16);
+                              ((split * MT * NT + i * NT + s) * NTH + (int)threadIdx.x) * 16);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __shared__ int last;
     __syncthreads();
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(256, 1) void gemm_int8_medium_kernel(
 #pragma unroll
         for (int s = 0; s < NT; ++s)
           sum[i][s] += __builtin_bit_cast(
-              f32x4_t, buf_load128_coherent(pbuf, ((q * MT * NT + i * NT + s) * 256 + (int)threadIdx.x) * 16));
+              f32x4_t, buf_load128_coherent(pbuf, ((q * MT * NT + i * NT + s) * NTH + (int)threadIdx.x) * 16));
     store_y(sum);
   }
 }
@@ -274,30 +277,32 @@ __global__ __launch_bounds__(256, 1) void gemm_int8_medium_kernel(
 // stages in flight per workgroup
 constexpr int kMediumDepth = 4;
 
-size_t medium_workspace_bytes(int tiles, int splits, int mt, int nt) {
+size_t medium_workspace_bytes(int tiles, int splits, int mt, int strips_per_wg) {
   if (splits <= 1) return 0;
-  return (size_t)((tiles + 63) & ~63) * 4 + (size_t)tiles * splits * mt * nt * 256 * 16;
+  return (size_t)((tiles + 63) & ~63) * 4 + (size_t)tiles * splits * mt * strips_per_wg * 64 * 16;
 }
 
-template <int XDT, int MT, int NT>
+template <int XDT, int MT, int NT, int WV>
 static hipError_t launch_medium_nt(const MatmulArgs& a, const GemmPlan& p) {
   const unsigned tiles = (unsigned)(p.n_tiles * p.m_tiles);
   if (p.splits > 1)
-    return launch_kernel(gemm_int8_medium_kernel<XDT, MT, NT, kMediumDepth, true>, dim3(tiles * p.splits),
-                         dim3(256), a.stream, a.x, a.Q, a.scales, a.y, a.workspace, a.M, a.N,
-                         a.K, pack_tiles(p.n_tiles, a.y_dtype, false, p.splits));
-  return launch_kernel(gemm_int8_medium_kernel<XDT, MT, NT, kMediumDepth, false>, dim3(tiles), dim3(256),
-                       a.stream, a.x, a.Q, a.scales, a.y, nullptr, a.M, a.N, a.K,
+    return launch_kernel(gemm_int8_medium_kernel<XDT, MT, NT, WV, kMediumDepth, true>,
+                         dim3(tiles * p.splits), dim3(64 * WV), a.stream, a.x, a.Q, a.scales, a.y,
+                         a.workspace, a.M, a.N, a.K, pack_tiles(p.n_tiles, a.y_dtype, false, p.splits));
+  return launch_kernel(gemm_int8_medium_kernel<XDT, MT, NT, WV, kMediumDepth, false>, dim3(tiles),
+                       dim3(64 * WV), a.stream, a.x, a.Q, a.scales, a.y, nullptr, a.M, a.N, a.K,
                        pack_tiles(p.n_tiles, a.y_dtype, false));
 }
 
 template <int XDT>
 static hipError_t launch_medium_x(const MatmulArgs& a, const GemmPlan& p) {
   const int mt = p.mtile / 16;
-  if (mt == 2 && p.nt == 2) return launch_medium_nt<XDT, 2, 2>(a, p);
-  if (mt == 2 && p.nt == 4) return launch_medium_nt<XDT, 2, 4>(a, p);
-  if (mt == 4 && p.nt == 2) return launch_medium_nt<XDT, 4, 2>(a, p);
-  if (mt == 4 && p.nt == 4) return launch_medium_nt<XDT, 4, 4>(a, p);
+  if (p.waves == 8 && p.nt == 1)
+    return mt == 2 ? launch_medium_nt<XDT, 2, 1, 8>(a, p) : launch_medium_nt<XDT, 4, 1, 8>(a, p);
+  if (p.waves == 4 && p.nt == 2)
+    return mt == 2 ? launch_medium_nt<XDT, 2, 2, 4>(a, p) : launch_medium_nt<XDT, 4, 2, 4>(a, p);
+  if (p.waves == 4 && p.nt == 4)
+    return mt == 2 ? launch_medium_nt<XDT, 2, 4, 4>(a, p) : launch_medium_nt<XDT, 4, 4, 4>(a, p);
   return hipErrorInvalidValue;
 }
 

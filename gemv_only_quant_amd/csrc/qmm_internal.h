@@ -100,8 +100,8 @@ hipError_t launch_gemm_large(const MatmulArgs& a, const GemmPlan& p);
 
 // ---- int8 MFMA GEMM at medium M (gemm_medium.hip) --------------------------
 // Workspace of a plan of `tiles` tiles split `splits` ways: tickets, then the
-// partial tiles (mt 16-row tiles x 4 nt strips per workgroup).
-size_t medium_workspace_bytes(int tiles, int splits, int mt, int nt);
+// partial tiles (mt 16-row tiles x strips_per_wg 16-column strips each).
+size_t medium_workspace_bytes(int tiles, int splits, int mt, int strips_per_wg);
 hipError_t launch_gemm_medium(const MatmulArgs& a, const GemmPlan& p);
 
 // ---- int8 x ternary (ternary.hip) -----------------------------------------
