@@ -22,7 +22,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-fvisibility=hidden", "-Wall", "-Wno-unused-result", "-Wno-unknown-pragmas",
           "-I", os.path.join(ROOT, "include")]
 SOURCES = ["qmm_api.cpp", "gemv_lowbit.hip", "gemv_tile.hip", "gemv_int8.hip", "repack.hip",
-           "gemm_mfma.hip", "gemm_large.hip", "gemm_medium.hip", "ternary.hip", "quantize.hip"]
+           "gemm_mfma.hip", "gemm_large.hip", "gemm_medium.hip", "ternary.hip", "ternary_large.hip",
+           "quantize.hip"]
 
 
 def _stale(src, obj):

@@ -444,6 +444,9 @@ qmm_status qmm_i8t2_gemm(const void* x, const void* W_tile, int32_t* y, int M, i
   qmm_status st = t2_shape(fn, N, K, &noop);
   if (st != QMM_OK) return st;
   if (noop || M == 0) return ok();
+  // large M: 32-bit buffer offsets span a 256-row tile of x (256 K bytes)
+  if (M > 64 && K >= (1 << 23))
+    return fail(QMM_ERR_UNSUPPORTED, "%s: K=%d too large for M > 64 (K < 2^23)", fn, K);
   if (x == nullptr || W_tile == nullptr || y == nullptr)
     return fail(QMM_ERR_ARG, "%s: NULL x, W_tile or y", fn);
   if (!aligned16(x) || !aligned16(W_tile) || !aligned16(y))

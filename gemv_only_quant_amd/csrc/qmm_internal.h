@@ -109,6 +109,9 @@ hipError_t launch_t2_pack(const void* Wp, void* Wt, int N, int K, hipStream_t s)
 hipError_t launch_t2_unpack(const void* Wt, void* Wp, int N, int K, hipStream_t s);
 hipError_t launch_i8t2_gemm(const void* x, const void* Wt, int32_t* y, int M, int N, int K,
                             hipStream_t s);
+// large M (ternary_large.hip): 256-row tiles, the column split of large_split
+hipError_t launch_i8t2_large(const void* x, const void* Wt, int32_t* y, int M, int N, int K,
+                             hipStream_t s);
 
 // ---- round-to-nearest quantizer (quantize.hip) -----------------------------
 hipError_t launch_quantize(const void* W, int w_dtype, void* qw, void* scales, void* qzeros,

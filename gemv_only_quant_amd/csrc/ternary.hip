@@ -18,9 +18,11 @@
 //    the B operand of v_mfma_i32_16x16x64_i8 directly (the x operand uses the
 //    same k order per lane group, so products pair up whatever order the
 //    instruction sums in);
-//  * x tiles go global -> LDS (global_load_lds_dwordx4), double-buffered and
-//    fragment-major (one 1 KiB block per 16 rows x 64 k), so every A operand
-//    is one conflict-free ds_read_b128; the sums are exact int32.
+//  * x reaches the A operands through LDS tiles in a swizzled row layout
+//    (whole rows per load, conflict-free ds_read_b128 fragments); the sums
+//    are exact int32.
+// This file holds the repack, the decode kernel (M <= 16) and the 16-row
+// tile kernel (17-64 rows); ternary_large.hip the 256-row one.
 #include <hip/hip_runtime.h>
 
 #include "qmm_device.h"
@@ -95,7 +97,9 @@ __device__ __forceinline__ void mfma_i8_acc(i32x4_t& c, const u32x4_t& a, const 
 }
 
 // Workgroup tile 16 MT rows x 64 NT4 columns: 4 waves side by side along N,
-// each NT4 strips of 16 columns, MT 16-row tiles; 256-deep stages.
+// each NT4 strips of 16 columns, MT 16-row tiles; 256-deep stages.  Used at
+// 17-64 rows (MT = NT4 = 1); larger M goes to the 256-row kernel of
+// ternary_large.hip.
 template <int MT, int NT4>
 __global__ __launch_bounds__(256) void i8t2_gemm_kernel(const int8_t* __restrict__ x,
                                                         const u32x4_t* __restrict__ Wt,
@@ -225,45 +229,18 @@ __global__ __launch_bounds__(256) void i8t2_gemm_kernel(const int8_t* __restrict
     for (int s = 0; s < NT4; ++s) asm volatile("" : "+a"(acc[i][s]));
   __builtin_amdgcn_sched_barrier(0);
 
-  if constexpr (NT4 == 4) {
-    // y through LDS per 16-row tile, as the low-bit prefill does: the
-    // wave's 16 x 64 block goes in row-major (row stride 68 words, no bank
-    // conflicts either way) and leaves as 4 whole rows per store
-    // instruction (16 lanes x 16 bytes per row), i.e. whole 128-byte lines.
-    // The x buffers are free (the K loop ended with a barrier).
-    int32_t* const yl = reinterpret_cast<int32_t*>(&xa[0][0]) + wave * (16 * 68);
-    const int prow = lane >> 4, pcol = 4 * (lane & 15);
-    const bool pcol_ok = s0 + ((lane & 15) >> 2) < strips;
+  // each lane stores its accumulator elements (4 rows of one column)
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
+  for (int s = 0; s < NT4; ++s) {
+    if (s0 + s >= strips) continue;
+    const int n = 16 * (s0 + s) + l16;
 #pragma unroll
-      for (int s = 0; s < NT4; ++s)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) yl[(4 * quad + r) * 68 + 16 * s + l16] = acc[i][s][r];
-      i32x4_t v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        v[j] = *reinterpret_cast<const i32x4_t*>(yl + (4 * j + prow) * 68 + pcol);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int m = m0 + 16 * i + 4 * j + prow;
-        if (m < M && pcol_ok)
-          *reinterpret_cast<i32x4_t*>(y + (size_t)m * N + 16 * s0 + pcol) = v[j];
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 16 * i + 4 * quad + r;
+        if (m < M) y[(size_t)m * N + n] = acc[i][s][r];
       }
-    }
-  } else {
-#pragma unroll
-    for (int s = 0; s < NT4; ++s) {
-      if (s0 + s >= strips) continue;
-      const int n = 16 * (s0 + s) + l16;
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + 16 * i + 4 * quad + r;
-          if (m < M) y[(size_t)m * N + n] = acc[i][s][r];
-        }
-    }
   }
 }
 
@@ -379,8 +356,8 @@ hipError_t launch_i8t2_gemm(const void* x, const void* Wt, int32_t* y, int M, in
     return launch_kernel(i8t2_skinny_kernel<1>, dim3((unsigned)n_tiles), dim3(256), st, x, Wt, y,
                          M, N, K, n_tiles);
   }
-  if (M <= 64) return launch_i8t2<1, 1>(x, Wt, y, M, N, K, st);
-  return launch_i8t2<8, 4>(x, Wt, y, M, N, K, st);
+  if (M <= 64) return launch_i8t2<1, 1>(x, Wt, y, M, N, K, st);  // 16-row tiles
+  return launch_i8t2_large(x, Wt, y, M, N, K, st);
 }
 
 }  // namespace qmm

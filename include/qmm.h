@@ -243,7 +243,8 @@ QMM_API qmm_status qmm_t2_unpack_layout(const void* W_tile, void* W_page, int N,
  * qmm_i8t2_gemm: y = x * W on the int8 matrix cores, W in the tile layout;
  * any M >= 1, N % 16 == 0, K % 256 == 0; y fully overwritten.  The sums are
  * exact for K < 2^23 (|x w| <= 256); larger K wraps as the page's int32
- * accumulator would.
+ * accumulator would.  For M > 64, K must be below 2^23 (QMM_ERR_UNSUPPORTED
+ * otherwise).
  */
 QMM_API qmm_status qmm_i8t2_gemm(const void* x, const void* W_tile, int32_t* y, int M, int N,
                                  int K, void* stream);

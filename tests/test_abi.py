@@ -175,6 +175,7 @@ def test_ternary_calls_reject():
     assert L.qmm_i8t2_gemm(A, A, None, 4, 64, 256, 0) == E_ARG
     assert L.qmm_i8t2_gemm(A, A, MIS, 4, 64, 256, 0) == E_ARG
     assert L.qmm_i8t2_gemm(A, A, A, 4, 64, 320, 0) == E_UNS
+    assert L.qmm_i8t2_gemm(A, A, A, 65, 64, 1 << 23, 0) == E_UNS and "M > 64" in qmm.qmm_last_error()
     assert L.qmm_i8t2_gemm(None, None, None, 0, 64, 256, 0) == qmm.QMM_OK   # M = 0
 
 

@@ -46,15 +46,31 @@ def test_i8t2_exact(M, N, K):
     assert np.array_equal(run(case), oracle.i8t2_mm(case.A.numpy(), case.Wp.numpy(), M, N, K))
 
 
+# 256-row tiles: one or two of them with ragged rows and strips, and at
+# full height a plan of 256-column tiles followed by 192-column ones (at
+# N = 4352: 16 x 16 full tiles, then 2 narrow ones, the second one past N).
+LARGE = [  # M, N, K
+    (65, 48, 256), (300, 272, 768), (513, 1040, 512), (4096, 4352, 256),
+]
+
+
+@pytest.mark.parametrize("M,N,K", LARGE)
+def test_i8t2_large_exact(M, N, K):
+    case = si.t2_case(M, N, K, seed=M + 3 * N + K, codes=4)
+    want = oracle.i8t2_mm_mt(case.A.numpy(), case.Wp.numpy(), M, N, K)
+    assert np.array_equal(run(case), want)
+
+
 @pytest.mark.parametrize("M,N,K", [(3, 32, 512), (70, 64, 256)])
 def test_i8t2_code_three_reads_as_two(M, N, K):
     case = si.t2_case(M, N, K, seed=M + K, codes=4)
     assert np.array_equal(run(case), oracle.i8t2_mm(case.A.numpy(), case.Wp.numpy(), M, N, K))
 
 
+@pytest.mark.parametrize("M", [20, 300])
 @pytest.mark.parametrize("code,want", [(2, -128), (0, 128), (3, -256)])
-def test_i8t2_extremes(code, want):
-    M, N, K = 20, 32, 4096
+def test_i8t2_extremes(code, want, M):
+    N, K = 32, 4096
     A = torch.full((M, K), -128, dtype=torch.int8)
     Wp = torch.full((K // 4, N), code * 0b01010101, dtype=torch.uint8)
     case = si.T2Case("extreme", M, N, K, A, Wp)
