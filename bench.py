@@ -528,7 +528,10 @@ def phases(launches=200):
     build.py --phases), beside the same stamps on a read-only kernel with
     the same grid reading the same bytes per workgroup.  Each launch runs on
     its own weight copy (a pool of >= 512 MB) after the previous one has
-    finished, and its stamps are read back before the next."""
+    finished, and its stamps are read back before the next.  Then both
+    kernels graph-replayed back to back over the pool (the read-only one
+    gives the best this launch shape does with no arithmetic), and the
+    matrix cores' sustained bf16 and int8 rates on register operands."""
     import ctypes
     import torch
     import gemv_only_quant_amd as qmm
@@ -597,33 +600,70 @@ def phases(launches=200):
                    7: "half_blocks_done_us", 3: "weights_consumed_us", 4: "scales_in_lds_us"})
     r = run(readonly, {3: "last_load_returned_us"})
 
-    # the matrix cores' sustained rate: 8 independent bf16 MFMAs per round on
+    # graph-replayed back to back over the pool (the bench's own timing), the
+    # GEMV and the read-only kernel of the same grid: the read rate this
+    # launch shape reaches at best, with no arithmetic at all
+    def replayed(fn, label, steps=200):
+        for i in range(10):
+            fn(i)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(steps):
+                fn(i)
+        graph.replay()
+        torch.cuda.synchronize()
+        us = replay_us(graph, steps, label)
+        del graph
+        return {"us_per_call": round(us, 3), "read_TBps": round(wbytes / us / 1e6, 3)}
+
+    cur = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731 (the capture stream)
+
+    def gemv_cur(i):
+        assert lib.qmm_gemm(d.x.data_ptr(), pool[i % copies].data_ptr(), d.scales.data_ptr(),
+                            d.zeros.data_ptr(), y.data_ptr(), case.M, case.N, case.K, case.w_bit,
+                            case.group_size, x_dt, None, 0, cur()) == 0
+
+    def readonly_cur(i):
+        assert lib.qmm_phase_readonly(pool[i % copies].data_ptr(), sink.data_ptr(),
+                                      case.N // 16, nblk, cur()) == 0
+
+    rep = {"tile_gemv_stamp_build": replayed(gemv_cur, "phases gemv"),
+           "read_only_same_grid": replayed(readonly_cur, "phases read-only")}
+
+    # the matrix cores' sustained rate: 8 independent MFMAs per round on
     # register operands, 4 workgroups per CU, zero and random operands
-    lib.qmm_calib_mfma.argtypes = [vp, vp, ci, ci, vp]
+    lib.qmm_calib_mfma.argtypes = [vp, vp, ci, ci, ci, vp]
     lib.qmm_calib_mfma.restype = ci
     blocks, iters = 1024, 20000
     sink2 = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
-    mfma = {}
     gen = torch.Generator().manual_seed(5)
-    for label, seed in (("zero_operands", torch.zeros(128 * 8, dtype=torch.bfloat16)),
-                        ("random_operands", torch.randn(128 * 8, generator=gen).to(torch.bfloat16))):
-        sd = seed.to("cuda")
-        assert lib.qmm_calib_mfma(sd.data_ptr(), sink2.data_ptr(), blocks, 100, stream) == 0
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        assert lib.qmm_calib_mfma(sd.data_ptr(), sink2.data_ptr(), blocks, iters, stream) == 0
-        ev1.record()
-        torch.cuda.synchronize()
-        secs = ev0.elapsed_time(ev1) * 1e-3
-        flops = blocks * 4 * iters * 8 * 2.0 * 16 * 16 * 32
-        mfma[label] = {"ms": round(secs * 1e3, 3), "tflops": round(flops / secs / 1e12, 1),
-                       "frac_of_2500": round(flops / secs / 1e12 / MFMA_PEAK_TFLOPS, 4)}
-    # the same harness's graph-replayed time, for the launch floor
+    loops = {}
+    for kind, int8, peak in (("bf16_16x16x32", 0, MFMA_PEAK_TFLOPS),
+                             ("int8_16x16x64", 1, INT8_PEAK_TOPS)):
+        rnd = (torch.randint(-128, 128, (2048,), generator=gen, dtype=torch.int8) if int8 else
+               torch.randn(128 * 8, generator=gen).to(torch.bfloat16))
+        res = {}
+        for label, seed in (("zero_operands", torch.zeros_like(rnd)), ("random_operands", rnd)):
+            sd = seed.to("cuda")
+            assert lib.qmm_calib_mfma(sd.data_ptr(), sink2.data_ptr(), blocks, 100, int8,
+                                      stream) == 0
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            assert lib.qmm_calib_mfma(sd.data_ptr(), sink2.data_ptr(), blocks, iters, int8,
+                                      stream) == 0
+            ev1.record()
+            torch.cuda.synchronize()
+            secs = ev0.elapsed_time(ev1) * 1e-3
+            ops = blocks * 4 * iters * 8 * 2.0 * 16 * 16 * (64 if int8 else 32)
+            res[label] = {"ms": round(secs * 1e3, 3), "tops": round(ops / secs / 1e12, 1),
+                          "frac_of_peak": round(ops / secs / 1e12 / peak, 4)}
+        loops["mfma_loop_" + kind] = dict(res, peak=peak)
     out = {"workload": HEADLINE, "launches": launches, "stamp_clock": "s_memrealtime, 100 MHz",
-           "tile_gemv": g, "read_only_same_grid": r,
-           "mfma_loop_bf16_16x16x32": dict(mfma, blocks=blocks, waves_per_block=4,
-                                           rounds=iters, mfma_per_round=8)}
+           "tile_gemv": g, "read_only_same_grid": r, "graph_replayed": rep,
+           "mfma_loops": dict(loops, blocks=blocks, waves_per_block=4, rounds=iters,
+                              mfma_per_round=8)}
     print(json.dumps(out), flush=True)
     return out
 
