@@ -64,7 +64,7 @@ template <int W_BIT, int XDT> struct Pairs {
 // points of the kernel into a device array the host reads back.  Stamp
 // slots per wave: 0 entry, 1 x slice and its sums in LDS, 2 group-sum table
 // ready, 3 every weight block's dot products done (its loads returned),
-// 4 scales and zero words in LDS, 5 output stored, 6 the first block's dot
+// 4 scales and zero words ready (in LDS, where they go through it), 5 output stored, 6 the first block's dot
 // products done, 7 the first half of the blocks' done.
 #ifdef QMM_PHASE_STAMPS
 constexpr int kStampSlots = 8;
@@ -127,9 +127,14 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t xl[MB * PASS_K];
   __shared__ __attribute__((aligned(16))) float xsum[MB * PO * NS];
   __shared__ __attribute__((aligned(16))) float2 gtab[2][TE];
-  __shared__ uint16_t sl[GPP * 16];
-  __shared__ uint32_t zl[ZR * 16];
-  __shared__ float red[WV][MB][16];
+  // DIRECT: each lane loads the scales and zero words of its own blocks'
+  // groups straight into registers (at most 8 of each), so the epilogue
+  // needs neither an LDS exchange nor a barrier for them; otherwise they go
+  // through LDS cooperatively
+  constexpr bool DIRECT = NBW * SPB <= 8;
+  __shared__ uint16_t sl[DIRECT ? 1 : GPP * 16];
+  __shared__ uint32_t zl[DIRECT ? 1 : ZR * 16];
+  __shared__ float red[WV][4][MB][16];  // per wave and k-octet lane group
 
   // descriptors: a block past the strip, a row past M, a group past G read 0
   const buf_t qbuf = make_buf(Qt + (size_t)s * nblk * 64, (uint32_t)nblk * 1024u);
@@ -175,17 +180,29 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
 
     // scales and zero words last: only the pass's closing epilogue reads
     // them, so no dot product waits for them (loads complete in order)
-    uint32_t su[SU], zu[ZU];
+    uint32_t su[DIRECT ? 1 : SU], zu[DIRECT ? 1 : ZU];
+    uint32_t sd[DIRECT ? NBW * SPB : 1], zd[DIRECT ? NBW * SPB : 1];
+    if constexpr (DIRECT) {
 #pragma unroll
-    for (int j = 0; j < SU; ++j) {
-      const int u = threadIdx.x + NTH * j;
-      const int gl = u >> 3, cp = u & 7;
-      su[j] = buf_load32(sbuf, u < GPP * 8 ? ((gp0 + gl) * N + 2 * cp) * 2 : OUT);
-    }
+      for (int i = 0; i < NBW; ++i)
 #pragma unroll
-    for (int j = 0; j < ZU; ++j) {
-      const int u = threadIdx.x + NTH * j;
-      zu[j] = buf_load32(zbuf, u < ZR * 16 ? ((zr0 + (u >> 4)) * N + (u & 15)) * 4 : OUT);
+        for (int e = 0; e < SPB; ++e) {
+          const int g = ((((kb0 + i) * KB) >> gsh) & gmask) + e;
+          sd[i * SPB + e] = buf_load16(sbuf, (g * N + col) * 2);
+          zd[i * SPB + e] = buf_load32(zbuf, ((g / PACK) * N + col) * 4);
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < SU; ++j) {
+        const int u = threadIdx.x + NTH * j;
+        const int gl = u >> 3, cp = u & 7;
+        su[j] = buf_load32(sbuf, u < GPP * 8 ? ((gp0 + gl) * N + 2 * cp) * 2 : OUT);
+      }
+#pragma unroll
+      for (int j = 0; j < ZU; ++j) {
+        const int u = threadIdx.x + NTH * j;
+        zu[j] = buf_load32(zbuf, u < ZR * 16 ? ((zr0 + (u >> 4)) * N + (u & 15)) * 4 : OUT);
+      }
     }
     // 3. the pass to LDS
     if (k0 > 0) __syncthreads();  // the previous pass is done reading
@@ -320,19 +337,21 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
 
     // 5. the pass's scales and zero words to LDS (the x slice and group table
     // are no longer written; every wave is past the table reads of step 3)
-#pragma unroll
-    for (int j = 0; j < SU; ++j) {
-      const int u = threadIdx.x + NTH * j;
-      if (u < GPP * 8) reinterpret_cast<uint32_t*>(sl)[u] = su[j];
-    }
     // symmetric: every zero field holds 2^(w_bit-1) (the descriptor read 0)
     const uint32_t zfill = zp ? 0u : (W_BIT == 4 ? 0x88888888u : 0xAAAAAAAAu);
+    if constexpr (!DIRECT) {
 #pragma unroll
-    for (int j = 0; j < ZU; ++j) {
-      const int u = threadIdx.x + NTH * j;
-      if (u < ZR * 16) zl[u] = zu[j] | zfill;
+      for (int j = 0; j < SU; ++j) {
+        const int u = threadIdx.x + NTH * j;
+        if (u < GPP * 8) reinterpret_cast<uint32_t*>(sl)[u] = su[j];
+      }
+#pragma unroll
+      for (int j = 0; j < ZU; ++j) {
+        const int u = threadIdx.x + NTH * j;
+        if (u < ZR * 16) zl[u] = zu[j] | zfill;
+      }
+      __syncthreads();
     }
-    __syncthreads();
     QMM_STAMP(4);
 
     // 6. group epilogue: r += s (sum x (B + q) - B X - z X), where the
@@ -346,8 +365,10 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
 #pragma unroll
       for (int e = 0; e < SPB; ++e) {
         const int g = g0 + e;
-        const float sv = f16_bits_to_f32(sl[(g - gp0) * 16 + col]);
-        const float zf = (float)((zl[(g / PACK - zr0) * 16 + col] >> ((g % PACK) * W_BIT)) & ZMASK);
+        const float sv = f16_bits_to_f32(DIRECT ? (uint16_t)sd[i * SPB + e]
+                                                : sl[(g - gp0) * 16 + col]);
+        const uint32_t zw = DIRECT ? zd[i * SPB + e] | zfill : zl[(g / PACK - zr0) * 16 + col];
+        const float zf = (float)((zw >> ((g % PACK) * W_BIT)) & ZMASK);
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
           const float2 pe = gtab[oct != 0][(m * WV * NBW + (kb - k0 / KB)) * SPB + e];
@@ -357,27 +378,21 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
     }
   }
 
-  // 5. the column's 4 k-octet lanes (L, L+16, L+32, L+48), then the waves
+  // 7. every lane's partial to LDS; one thread per output adds the column's
+  // 4 k-octet lanes of every wave (one LDS round trip, no shuffles)
 #pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    float v = r[m];
-    v += __shfl_xor(v, 16);
-    v += __shfl_xor(v, 32);
-    r[m] = v;
-  }
-  if (lane < 16) {
-#pragma unroll
-    for (int m = 0; m < MB; ++m) red[wave][m][lane] = r[m];
-  }
+  for (int m = 0; m < MB; ++m) red[wave][oct][m][col] = r[m];
   __syncthreads();
   auto store = [&](auto* yt) {
     using T = typename std::remove_pointer<decltype(yt)>::type;
     if (threadIdx.x < 16 * MB) {
       const int m = threadIdx.x >> 4, c = threadIdx.x & 15;
       if (m < M) {
-        float sum = red[0][m][c];
+        float sum = 0.f;
 #pragma unroll
-        for (int v = 1; v < WV; ++v) sum += red[v][m][c];
+        for (int v = 0; v < WV; ++v)
+#pragma unroll
+          for (int o = 0; o < 4; ++o) sum += red[v][o][m][c];
         yt[(size_t)m * N + 16 * s + c] = (T)sum;
       }
     }
