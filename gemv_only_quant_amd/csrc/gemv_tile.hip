@@ -64,8 +64,9 @@ template <int W_BIT, int XDT> struct Pairs {
 // points of the kernel into a device array the host reads back.  Stamp
 // slots per wave: 0 entry, 1 x slice and its sums in LDS, 2 group-sum table
 // ready, 3 every weight block's dot products done (its loads returned),
-// 4 scales and zero words ready (in LDS, where they go through it), 5 output stored, 6 the first block's dot
-// products done, 7 the first half of the blocks' done.
+// 4 scales and zero words ready (in LDS, where they go through it),
+// 5 output stored, 6 the first block's dot products done, 7 the first half
+// of the blocks' done.
 #ifdef QMM_PHASE_STAMPS
 constexpr int kStampSlots = 8;
 constexpr int kStampWaves = 4 * 8192;  // up to 8192 workgroups of 4 waves
