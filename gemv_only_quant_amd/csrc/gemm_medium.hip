@@ -156,6 +156,15 @@ __global__ __launch_bounds__(64 * WV, 1) void gemm_int8_medium_kernel(
   // buffer t % 2 at the top of the stage, then one barrier: every wave has
   // written its units of stage t and finished reading stage t - 1, whose
   // buffer stage t + 1 reuses.
+  // column scales of the wave's strips (past N: zeros, never stored),
+  // requested before the weights so that their latency overlaps the K
+  // loop's instead of following it
+  const buf_t sb = make_buf(scales + 16 * sc0, (uint32_t)(nvalid * 16 * 4));
+  float sc[NT];
+#pragma unroll
+  for (int s = 0; s < NT; ++s)
+    sc[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sb, (16 * s + l16) * 4, 0, 0));
+  __builtin_amdgcn_sched_barrier(0);
   WRegs ring[D];
   auto issue = [&](int t, int d) {
 #pragma unroll
@@ -200,12 +209,6 @@ __global__ __launch_bounds__(64 * WV, 1) void gemm_int8_medium_kernel(
     }
   }
 
-  // column scales of the wave's strips (past N: zeros, never stored)
-  const buf_t sb = make_buf(scales + 16 * sc0, (uint32_t)(nvalid * 16 * 4));
-  float sc[NT];
-#pragma unroll
-  for (int s = 0; s < NT; ++s)
-    sc[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sb, (16 * s + l16) * 4, 0, 0));
 
   auto store_y = [&](const f32x4_t (&v)[MT][NT]) {
     with_y(y, ydt, [&](auto* yt) {

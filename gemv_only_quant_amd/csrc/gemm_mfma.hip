@@ -282,6 +282,14 @@ __device__ __forceinline__ void skinny_body(
     }
   };
 
+  // int8 column scales, requested before the weights so that their latency
+  // overlaps the K loop's instead of following it
+  float csc[LOWBIT ? 1 : NT];
+  if constexpr (!LOWBIT) {
+#pragma unroll
+    for (int s = 0; s < NT; ++s)
+      csc[s] = reinterpret_cast<const float*>(scales)[16 * min(s0 + s, strips - 1) + l16];
+  }
   // DEPTH-deep ring of stages in registers: stage st + DEPTH is requested
   // while stage st computes (loads past the range re-read its last stage)
   if (st0 < st1) {
@@ -302,13 +310,10 @@ __device__ __forceinline__ void skinny_body(
     }
   }
   if constexpr (!LOWBIT) {
-    float sc[NT], bz[NT];
+    float bz[NT];
 #pragma unroll
-    for (int s = 0; s < NT; ++s) {
-      sc[s] = reinterpret_cast<const float*>(scales)[16 * min(s0 + s, strips - 1) + l16];
-      bz[s] = CB;
-    }
-    flush(sc, bz);
+    for (int s = 0; s < NT; ++s) bz[s] = CB;
+    flush(csc, bz);
   }
 
   // ---- the waves' K ranges meet in LDS (over the x tiles: wait for all) ---

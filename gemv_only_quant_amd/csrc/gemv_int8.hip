@@ -52,9 +52,12 @@ __global__ __launch_bounds__(256) void gemv_int8_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ Q,
     const float* __restrict__ scale, void* __restrict__ y, int ydt, int M, int N, int K) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int n0 = (blockIdx.x * 4 + wave) * RN;
   if (n0 >= N) return;
+  float sc[RN];
+#pragma unroll
+  for (int r = 0; r < RN; ++r) sc[r] = 0.f;
 
   float acc[MB][RN];
   float xs[MB];
@@ -74,6 +77,16 @@ __global__ __launch_bounds__(256) void gemv_int8_kernel(
       q[r] = (kok && n0 + r < N)
                  ? *reinterpret_cast<const u32x4_t*>(Q + (size_t)(n0 + r) * K + k)
                  : u32x4_t{0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
+    // the rows' scales, loaded behind the first weights (loads return in
+    // order): their latency overlaps the weights' instead of following the
+    // reduction, and no weight waits for them
+    // (a vector load: a scalar one would be waited for with the kernel's
+    // other scalar loads; rows past N read 0)
+    if (kc == 0) {
+      const buf_t sb = make_buf(scale, (uint32_t)N * 4u);
+#pragma unroll
+      for (int r = 0; r < RN; ++r) sc[r] = __builtin_bit_cast(float, buf_load32(sb, (n0 + r) * 4));
+    }
     uint32_t wp[RN][8];
 #pragma unroll
     for (int r = 0; r < RN; ++r)
@@ -107,7 +120,7 @@ __global__ __launch_bounds__(256) void gemv_int8_kernel(
       for (int m = 0; m < MB; ++m)
 #pragma unroll
         for (int r = 0; r < RN; ++r)
-          if (m < M && n0 + r < N) yt[(size_t)m * N + n0 + r] = (T)(scale[n0 + r] * v[m][r]);
+          if (m < M && n0 + r < N) yt[(size_t)m * N + n0 + r] = (T)(sc[r] * v[m][r]);
     });
   }
 }
