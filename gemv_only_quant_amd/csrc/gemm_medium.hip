@@ -300,12 +300,18 @@ static hipError_t launch_medium_nt(const MatmulArgs& a, const GemmPlan& p) {
 template <int XDT>
 static hipError_t launch_medium_x(const MatmulArgs& a, const GemmPlan& p) {
   const int mt = p.mtile / 16;
-  if (p.waves == 8 && p.nt == 1)
+  if (p.waves == 8 && p.nt == 1) {
+    if (mt == 1) return hipErrorInvalidValue;  // 4 x units per stage: not 8 waves
     return mt == 2 ? launch_medium_nt<XDT, 2, 1, 8>(a, p) : launch_medium_nt<XDT, 4, 1, 8>(a, p);
+  }
   if (p.waves == 4 && p.nt == 2)
-    return mt == 2 ? launch_medium_nt<XDT, 2, 2, 4>(a, p) : launch_medium_nt<XDT, 4, 2, 4>(a, p);
+    return mt == 1   ? launch_medium_nt<XDT, 1, 2, 4>(a, p)
+           : mt == 2 ? launch_medium_nt<XDT, 2, 2, 4>(a, p)
+                     : launch_medium_nt<XDT, 4, 2, 4>(a, p);
   if (p.waves == 4 && p.nt == 4)
-    return mt == 2 ? launch_medium_nt<XDT, 2, 4, 4>(a, p) : launch_medium_nt<XDT, 4, 4, 4>(a, p);
+    return mt == 1   ? launch_medium_nt<XDT, 1, 4, 4>(a, p)
+           : mt == 2 ? launch_medium_nt<XDT, 2, 4, 4>(a, p)
+                     : launch_medium_nt<XDT, 4, 4, 4>(a, p);
   return hipErrorInvalidValue;
 }
 

@@ -456,21 +456,25 @@ GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size, bool with_wor
     p.workspace_bytes = 0;
     return p;
   }
-  // int8 at 17-64 rows: the medium kernel, whose workgroups cover 128
+  // int8 at 16-64 rows: the medium kernel, whose workgroups cover 128
   // columns and share their x rows through LDS (the skinny kernel's 64-column
   // workgroups each re-read all of x), K split over workgroups so that about
   // one round of them covers the CUs.  It needs the split's workspace unless
-  // the tiles alone fill the CUs.
+  // the tiles alone fill the CUs.  At 16 rows (K = 4096, N = 14336) it
+  // measured 16.3 us against the skinny kernel's 16.9 on the same box; below
+  // 16 rows the skinny kernel stays.
   static const int want_med = env_int("QMM_MEDIUM");
   static const int want_med_nt = env_int("QMM_MEDIUM_NT");
   static const int want_med_s = env_int("QMM_MEDIUM_SPLITS");
-  if (w_bit == 8 && M > 16 && M <= 64 && K % 128 == 0 && want_med != 0) {
-    const int mmt = M <= 32 ? 2 : 4;
+  static const int med_min = env_int("QMM_MEDIUM_MIN_M");
+  if (w_bit == 8 && M > (med_min >= 0 ? med_min : 15) && M <= 64 && K % 128 == 0 &&
+      want_med != 0) {
+    const int mmt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
     // 64 rows: 8 waves of one strip (two per SIMD) measured 21.8-22.2 us
     // against 24.2 for 4 waves of two strips; 32 rows: 4 waves (17.9-18.2
     // against 18.0-18.3)
     static const int want_med_w = env_int("QMM_MEDIUM_WAVES");
-    const int mw = (want_med_w == 4 || want_med_w == 8) ? want_med_w : (mmt == 4 ? 8 : 4);
+    const int mw = mmt == 1 ? 4 : (want_med_w == 4 || want_med_w == 8) ? want_med_w : (mmt == 4 ? 8 : 4);
     const int mnt = mw == 8 ? 1 : ((want_med_nt == 2 || want_med_nt == 4) ? want_med_nt : 2);
     const int n_tiles = (N / 16 + mw * mnt - 1) / (mw * mnt);
     const long tiles = n_tiles;

@@ -65,9 +65,11 @@ INT8 = [  # M, N, K, x_dtype
     (33, 32, 320, si.BF16),
     (64, 112, 1024, si.F16),
     (70, 16, 128, si.BF16),
-    # 17-64 rows with K % 128 == 0 take the medium kernel: ragged rows, a
+    # 16-64 rows with K % 128 == 0 take the medium kernel: ragged rows, a
     # last tile with 5 of its 8 strips, 9 stages split 5 + 4
     (50, 592, 1152, si.BF16),
+    # one 16-row tile: 17 strips over tiles of 8, 10 stages split 5 + 5
+    (16, 272, 1280, si.F16),
     # 33 stages over 8 splits of 5: the last split has none (its workgroup
     # adds an all-zero partial)
     (20, 64, 4224, si.F16),
@@ -99,8 +101,9 @@ def test_gemm_lowbit_exact_probe_bit_exact(M, N, K, w_bit, gs, xdt, sym):
                                         # odd count of 64-deep blocks: the last 128-deep
                                         # stage is half past K and its k steps are skipped
                                         (16, 32, 192, si.BF16), (33, 48, 320, si.F16),
-                                        # medium kernel: split 4 and 8 ways
-                                        (64, 112, 2048, si.BF16), (20, 64, 4224, si.F16)])
+                                        # medium kernel: split 4 and 8 ways, and at 16 rows
+                                        (64, 112, 2048, si.BF16), (20, 64, 4224, si.F16),
+                                        (16, 48, 640, si.BF16)])
 def test_gemm_int8_exact_probe_bit_exact(M, N, K, xdt):
     case = si.exact_int8_case(M, N, K, xdt, seed=N + 1)
     y = run_gemm(case)

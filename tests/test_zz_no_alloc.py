@@ -51,12 +51,12 @@ def test_noalloc_equals_gemm_ex_on_two_calls():
 @pytest.mark.gpu
 def test_noalloc_exact_probe_and_unsplit_shape():
     # exact arithmetic: bit-equal to the oracle; then a shape that needs no
-    # scratch at all (enough column tiles), int8
+    # scratch at all (200 column tiles of 128 fill the CUs unsplit), int8
     case = si.exact_lowbit_case(9, 32, 8192, 2, 64, si.F16, False, seed=82)
     y_ws, y_na = _both(case)
     assert np.array_equal(y_na.astype(np.float64), oracle.qmm(*case.oracle_args())[0])
-    case = si.int8_case(16, 4096, 1024, si.BF16, seed=83)
-    assert qmm.qmm_workspace_bytes(16, 4096, 1024, 8, 0) == 0
+    case = si.int8_case(16, 25600, 1024, si.BF16, seed=83)
+    assert qmm.qmm_workspace_bytes(16, 25600, 1024, 8, 0) == 0
     y_ws, y_na = _both(case)
     assert np.array_equal(y_ws, y_na)
 
