@@ -52,6 +52,9 @@ template <> __device__ __forceinline__ void mfma16_acc<XBF16>(f32x4_t& c, const 
 constexpr int kLargeMT = kLargeRows / 16;
 // eighths of a stage's row tiles over which its loads are issued
 constexpr int kLoadSpan = 4;
+// A fragments read from LDS ahead of the MFMAs that use them (int4 g128
+// M=4096 K=4096 N=11008: 3 measured 1% faster than 2, 4 no better than 3)
+constexpr int kFragAhead = 3;
 
 // s_waitcnt with vmcnt = 0 and the other counters at their maximum.
 static constexpr int kWaitVm0 = 0x0F70;
@@ -443,7 +446,7 @@ __device__ __forceinline__ void large_body(
     const u32x4_t* xs_buf = &xa[buf][0];
 
     // Software pipeline inside the stage: while the NT MFMAs of row tile i of
-    // k step k run, (1) the A fragment two tiles ahead is read from LDS,
+    // k step k run, (1) the A fragment kFragAhead tiles ahead is read from LDS,
     // (2) part of the next k step's B fragments is dequantized (the NT x 4
     // operand registers spread over the MT row tiles) -- in the last k step
     // those of the next stage, after its group constants -- and (3) part of
@@ -452,16 +455,20 @@ __device__ __forceinline__ void large_body(
     // conversion (and spills).
     // fragment (row tile i, k step kk) = slot 256 i + 16 l16 + ((4 kk + quad) ^ l16)
     auto afrag = [&](int i, int kk) { return xs_buf[256 * i + 16 * l16 + ((4 * kk + quad) ^ l16)]; };
-    u32x4_t a0 = afrag(0, 0);
-    u32x4_t a1 = afrag(1, 0);
+    constexpr int P = kFragAhead;
+    static_assert(P >= 1 && P <= STEPS * MT, "prefetch distance");
+    u32x4_t ar[P];
+#pragma unroll
+    for (int q = 0; q < P; ++q) ar[q] = afrag(q % MT, q / MT);
 #pragma unroll
     for (int k = 0; k < STEPS; ++k) {
       const int kn = k + 1;
       const int qn = GS < KS ? (32 * kn) / GS : 0;
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        const int t2 = k * MT + i + 2;  // fragment two ahead, in (k, i) order
-        u32x4_t an = a1;
+        const int t2 = k * MT + i + P;  // fragment P ahead, in (k, i) order
+        const u32x4_t a0 = ar[0];
+        u32x4_t an = ar[P - 1];
         if (t2 < STEPS * MT) an = afrag(t2 % MT, t2 / MT);
         // this row tile's operand register of the next k step (of the next
         // stage in the last k step), made between its MFMAs
@@ -494,8 +501,9 @@ __device__ __forceinline__ void large_body(
           if (j0 < j1) load_part(j0, stw, stn, buf ^ 1, nx2);
           if (j0 + 1 < j1) load_part(j0 + 1, stw, stn, buf ^ 1, nx2);
         }
-        a0 = a1;
-        a1 = an;
+#pragma unroll
+        for (int q = 0; q + 1 < P; ++q) ar[q] = ar[q + 1];
+        ar[P - 1] = an;
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll

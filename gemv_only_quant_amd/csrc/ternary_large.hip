@@ -34,6 +34,9 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kT2MT = kLargeRows / 16;  // 16-row tiles per workgroup
 constexpr int kT2Frags = kT2MT * 4;     // 1 KiB x units per 256-deep stage
 constexpr int kT2LoadSpan = 4;          // eighths of a stage's row tiles carrying its loads
+// A fragments read from LDS ahead of the MFMAs that use them (3 and 4
+// measured no faster than 2)
+constexpr int kT2FragAhead = 2;
 static constexpr int kT2WaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters at maximum
 
 __device__ __forceinline__ void mfma_i8(i32x4_t& c, const u32x4_t& a, const u32x4_t& b) {
@@ -188,15 +191,19 @@ __device__ __forceinline__ void i8t2_large_body(const int8_t* __restrict__ x,
     // tiles ahead is read from LDS, one operand register of the next k step
     // (of the next stage in the last k step) is made, and part of the next
     // stages' loads is issued.  The scheduling barriers hold this order.
-    u32x4_t a0 = afrag(0, 0);
-    u32x4_t a1 = afrag(1, 0);
+    constexpr int P = kT2FragAhead;
+    static_assert(P >= 1 && P <= STEPS * MT, "prefetch distance");
+    u32x4_t ar[P];
+#pragma unroll
+    for (int q = 0; q < P; ++q) ar[q] = afrag(q % MT, q / MT);
 #pragma unroll
     for (int k = 0; k < STEPS; ++k) {
       const int kn = k + 1;
 #pragma unroll
       for (int i = 0; i < MT; ++i) {
-        const int t2 = k * MT + i + 2;
-        u32x4_t an = a1;
+        const int t2 = k * MT + i + P;  // fragment P ahead, in (k, i) order
+        const u32x4_t a0 = ar[0];
+        u32x4_t an = ar[P - 1];
         if (t2 < STEPS * MT) an = afrag(t2 % MT, t2 / MT);
         const int r0 = i * NT * 4 / MT, r1 = (i + 1) * NT * 4 / MT;
         static_assert(NT * 4 <= MT, "one operand register per row tile at most");
@@ -217,8 +224,9 @@ __device__ __forceinline__ void i8t2_large_body(const int8_t* __restrict__ x,
           if (j0 < j1) load_part(j0, stw, stn, buf ^ 1, nx2);
           if (j0 + 1 < j1) load_part(j0 + 1, stw, stn, buf ^ 1, nx2);
         }
-        a0 = a1;
-        a1 = an;
+#pragma unroll
+        for (int q = 0; q + 1 < P; ++q) ar[q] = ar[q + 1];
+        ar[P - 1] = an;
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
