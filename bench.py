@@ -530,8 +530,9 @@ def phases(launches=200):
     its own weight copy (a pool of >= 512 MB) after the previous one has
     finished, and its stamps are read back before the next.  Then both
     kernels graph-replayed back to back over the pool (the read-only one
-    gives the best this launch shape does with no arithmetic), and the
-    matrix cores' sustained bf16 and int8 rates on register operands."""
+    gives the best this launch shape does with no arithmetic), the read-only
+    kernel with the GEMV's steps added one at a time, and the matrix cores'
+    sustained bf16 and int8 rates on register operands."""
     import ctypes
     import torch
     import gemv_only_quant_amd as qmm
@@ -630,6 +631,20 @@ def phases(launches=200):
 
     rep = {"tile_gemv_stamp_build": replayed(gemv_cur, "phases gemv"),
            "read_only_same_grid": replayed(readonly_cur, "phases read-only")}
+
+    # the read-only kernel with the GEMV's steps added one at a time
+    # (calibrate.hip, readonly_probe_kernel): which of them costs time
+    lib.qmm_calib_readonly.argtypes = [ci, vp, vp, vp, ci, vp]
+    lib.qmm_calib_readonly.restype = ci
+    assert nblk == 32 and d.x.numel() * d.x.element_size() >= 8192
+    probes = {}
+    for v, label in ((0, "loads_only"), (1, "x_slice"), (2, "per_block_dot_work"),
+                     (4, "closing_exchange"), (3, "x_slice+dot_work"), (7, "all_three")):
+        def probe_v(i, v=v):
+            assert lib.qmm_calib_readonly(v, pool[i % copies].data_ptr(), d.x.data_ptr(),
+                                          sink.data_ptr(), case.N // 16, cur()) == 0
+        probes[label] = replayed(probe_v, f"phases probe {label}")["us_per_call"]
+    rep["read_only_probes_us_per_call"] = probes
 
     # the matrix cores' sustained rate: 8 independent MFMAs per round on
     # register operands, 4 workgroups per CU, zero and random operands
