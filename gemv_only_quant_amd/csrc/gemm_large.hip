@@ -350,21 +350,30 @@ __device__ __forceinline__ void large_body(
       load_zero(s, st, R);
     }
   };
-  // Loads issued during a stage, one at a time: j < NWL are weight-side
-  // (slots, then scales, then zero words) of stage sw, the rest this wave's
-  // x fragments of stage sx.  The k loop issues them spread over its first
+  // Loads issued during a stage, one at a time: j < NXL are this wave's x
+  // fragments of stage sx, the rest weight-side (slots, then scales, then
+  // zero words) of stage sw.  The k loop issues them spread over its first
   // row tiles: a wave issues in order, so a burst of loads at the top of a
   // stage would hold its MFMAs back until the memory pipeline had taken
   // them all; what is issued late in the stage has little time left to land
   // before the stage's closing wait.
   constexpr int NWL = NT * (2 + NGS);
-  constexpr int NLD = NWL + FRAGS / 4;
+  constexpr int NXL = FRAGS / 4;
+  constexpr int NLD = NWL + NXL;
   auto load_part = [&](int j, int sw, int sx, int buf, WRegs& R) {
-    if (j < NT) load_slot(j, sw, R);
-    else if (j < NT + NT * NGS) load_scale((j - NT) / NGS, (j - NT) % NGS, sw, R);
-    else if (j < NWL) load_zero(j - NT - NT * NGS, sw, R);
-    else x_unit(j - NWL, sx, buf);
+    if (j < NXL) {
+      x_unit(j, sx, buf);
+    } else {
+      const int jw = j - NXL;
+      if (jw < NT) load_slot(jw, sw, R);
+      else if (jw < NT + NT * NGS) load_scale((jw - NT) / NGS, (jw - NT) % NGS, sw, R);
+      else load_zero(jw - NT - NT * NGS, sw, R);
+    }
   };
+  // A stage ends waiting for its x tile but not for the weight-side loads
+  // it issued after it (they are two stages ahead): vmcnt(NWL).
+  static_assert(NWL < 64, "vmcnt field");
+  constexpr int kWaitXTile = (NWL & 15) | ((NWL >> 4) << 14) | 0x0F70;
 
   f32x4_t acc[MT][NT];
 #pragma unroll
@@ -399,15 +408,17 @@ __device__ __forceinline__ void large_body(
   };
 
   // Weight registers of three stages: the current one, the next (loaded
-  // during the previous stage) and the one after (loading now).  The x
-  // tile of the next stage goes straight to LDS, and while such a load is
-  // in flight the compiler can only wait for every earlier load (vmcnt 0):
-  // loading weights two stages ahead lets the last k step read the next
-  // stage's weights, complete since the previous stage's closing wait.
-  WRegs cur, nx1, nx2;
+  // during the previous stage) and the one after (loading now).  A stage
+  // issues the next x tile's loads first and the weight side last, and
+  // ends waiting for the x tile only, so the weights it loaded have until
+  // the next stage's last k step (where the compiler waits for exactly
+  // them) to land.  The three sets take turns over an unrolled loop:
+  // moving registers from one set to another would make the compiler wait
+  // for their loads at the move.
+  WRegs ra, rb, rc;  // the three stages' roles rotate (no register copies)
   load_x(0, 0);
-  load_w(0, cur);
-  load_w(min(1, nst - 1), nx1);
+  load_w(0, ra);
+  load_w(min(1, nst - 1), rb);
   // pin the loads above the wait (the compiler may otherwise sink them
   // into the loop preheader, where they would still be in flight)
   auto pin = [](const WRegs& R) {
@@ -418,8 +429,8 @@ __device__ __forceinline__ void large_body(
       for (int q = 0; q < NGS; ++q) asm volatile("" ::"v"(R.sc[s][q]));
     }
   };
-  pin(cur);
-  pin(nx1);
+  pin(ra);
+  pin(rb);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
   // The first stage's group constants and first B fragment are made here;
@@ -429,12 +440,14 @@ __device__ __forceinline__ void large_body(
   u32x4_t b[NT], bn[NT];
 #pragma unroll
   for (int s = 0; s < NT; ++s) {
-    group_consts(cur, 0, s, gc[s]);
+    group_consts(ra, 0, s, gc[s]);
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      b[s][t] = bpair_scaled<W_BIT, XDT>(word_of(cur, s, 0, 0), 0, t, gc[s][0], hi_bits);
+      b[s][t] = bpair_scaled<W_BIT, XDT>(word_of(ra, s, 0, 0), 0, t, gc[s][0], hi_bits);
   }
-  for (int st = 0; st < nst; ++st) {
+  // One stage: cur holds its weights, nx1 the next stage's (loaded during
+  // the previous stage), nx2 receives the weights two stages ahead.
+  auto stage = [&](int st, const WRegs& cur, const WRegs& nx1, WRegs& nx2) {
     const int buf = st & 1;
     const int sub = W_BIT == 2 ? (st & 1) : 0;  // int2: which half of the 256-deep block
     // the next stage, loaded during this one (the last iteration re-reads
@@ -509,13 +522,18 @@ __device__ __forceinline__ void large_body(
 #pragma unroll
       for (int s = 0; s < NT; ++s) b[s] = bn[s];
     }
-    cur = nx1;
-    nx1 = nx2;
     // the next stage's x tile was written to LDS by the memory pipeline:
-    // wait for this wave's loads, then for every wave's
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    // wait for this wave's part of it (the weight-side loads issued after
+    // it may stay in flight), then for every wave's
+    __builtin_amdgcn_s_waitcnt(kWaitXTile);
     __syncthreads();
+  };
+  for (int st = 0; st < nst; st += 3) {
+    stage(st, ra, rb, rc);
+    if (st + 1 < nst) stage(st + 1, rb, rc, ra);
+    if (st + 2 < nst) stage(st + 2, rc, ra, rb);
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // the last re-reads of the final stage
   // the accumulators were last written by MFMAs the compiler does not see
   // as such: give them their result latency before they are read.  Each
   // accumulator then passes through an empty asm ordered after the wait, so
