@@ -138,13 +138,17 @@ __device__ __forceinline__ void i8t2_large_body(const int8_t* __restrict__ x,
 #pragma unroll
     for (int s = 0; s < NT; ++s) load_slot(s, st, R);
   };
-  // loads issued during a stage, one at a time: j < NT the weight slots of
-  // stage sw, the rest this wave's x units of stage sx
-  constexpr int NLD = NT + FRAGS / 4;
+  // loads issued during a stage, one at a time: j < NXL this wave's x units
+  // of stage sx, the rest the weight slots of stage sw.  A stage ends
+  // waiting for its x tile only (vmcnt(NT)): the weight slots issued after
+  // it, two stages ahead, may stay in flight.
+  constexpr int NXL = FRAGS / 4;
+  constexpr int NLD = NT + NXL;
   auto load_part = [&](int j, int sw, int sx, int buf, u32x4_t (&R)[NT]) {
-    if (j < NT) load_slot(j, sw, R);
-    else x_unit(j - NT, sx, buf);
+    if (j < NXL) x_unit(j, sx, buf);
+    else load_slot(j - NXL, sw, R);
   };
+  constexpr int kWaitXTile = (NT & 15) | 0x0F70;
 
   i32x4_t acc[MT][NT];
 #pragma unroll
@@ -153,17 +157,17 @@ __device__ __forceinline__ void i8t2_large_body(const int8_t* __restrict__ x,
     for (int s = 0; s < NT; ++s) acc[i][s] = i32x4_t{0, 0, 0, 0};
 
   // Weight registers of three stages: the current one, the next (loaded
-  // during the previous stage) and the one after (loading now).  While an
-  // x load to LDS is in flight the compiler can only wait for every earlier
-  // load, so the weights are loaded two stages ahead: the last k step then
-  // reads the next stage's words, complete since the previous stage's
-  // closing wait.
-  u32x4_t cur[NT], nx1[NT], nx2[NT];
+  // during the previous stage) and the one after (loading now); the last
+  // k step reads the next stage's words, where the compiler waits for
+  // exactly them.  The three sets take turns over an unrolled loop: moving
+  // registers from one set to another would make the compiler wait for
+  // their loads at the move.
+  u32x4_t ra[NT], rb[NT], rc[NT];
   load_x(0, 0);
-  load_w(0, cur);
-  load_w(min(1, nst - 1), nx1);
+  load_w(0, ra);
+  load_w(min(1, nst - 1), rb);
 #pragma unroll
-  for (int s = 0; s < NT; ++s) asm volatile("" ::"v"(cur[s]), "v"(nx1[s]));
+  for (int s = 0; s < NT; ++s) asm volatile("" ::"v"(ra[s]), "v"(rb[s]));
   __builtin_amdgcn_s_waitcnt(kT2WaitVm0);
   __syncthreads();
 
@@ -175,9 +179,10 @@ __device__ __forceinline__ void i8t2_large_body(const int8_t* __restrict__ x,
 #pragma unroll
   for (int s = 0; s < NT; ++s)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) b[s][t] = operand(cur[s][0], t);
+    for (int t = 0; t < 4; ++t) b[s][t] = operand(ra[s][0], t);
 
-  for (int st = 0; st < nst; ++st) {
+  auto stage = [&](int st, const u32x4_t (&cur)[NT], const u32x4_t (&nx1)[NT],
+                   u32x4_t (&nx2)[NT]) {
     const int buf = st & 1;
     // the last iterations re-read the final stage into the idle registers
     // and buffer, keeping the loop free of branches
@@ -232,16 +237,17 @@ __device__ __forceinline__ void i8t2_large_body(const int8_t* __restrict__ x,
 #pragma unroll
       for (int s = 0; s < NT; ++s) b[s] = bn[s];
     }
-#pragma unroll
-    for (int s = 0; s < NT; ++s) {
-      cur[s] = nx1[s];
-      nx1[s] = nx2[s];
-    }
     // the next stage's x tile was written to LDS by the memory pipeline:
-    // wait for this wave's loads, then for every wave's
-    __builtin_amdgcn_s_waitcnt(kT2WaitVm0);
+    // wait for this wave's part of it, then for every wave's
+    __builtin_amdgcn_s_waitcnt(kWaitXTile);
     __syncthreads();
+  };
+  for (int st = 0; st < nst; st += 3) {
+    stage(st, ra, rb, rc);
+    if (st + 1 < nst) stage(st + 1, rb, rc, ra);
+    if (st + 2 < nst) stage(st + 2, rc, ra, rb);
   }
+  __builtin_amdgcn_s_waitcnt(kT2WaitVm0);  // the last re-reads of the final stage
   // the accumulators were last written by MFMAs the compiler does not see
   // as such: give them their result latency, then pass each through an
   // empty asm ordered after that, so no read of one moves above it
