@@ -611,7 +611,7 @@ __global__ __launch_bounds__(256, 1) void gemm_large_kernel(
                                       full, xa);
   else
     large_body<W_BIT, XDT, GS, ZP, 3>(x, Qt, scales, qz, y, M, N, K, tail_tiles, ydt, gmask,
-                                      16 * n_full, b - full, (int)gridDim.x - full, xa);
+                                      16 * n_full, b - full, tail_tiles * m_tiles, xa);
 }
 
 // ---------------------------------------------------------------- host side

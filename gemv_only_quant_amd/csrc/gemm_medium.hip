@@ -96,7 +96,8 @@ __global__ __launch_bounds__(64 * WV, 1) void gemm_int8_medium_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, quad = lane >> 4;
   const int S = SPLIT ? splits_of(tile_opts) : 1;
-  const int w0 = xcd_remap(blockIdx.x, gridDim.x);
+  const int m_tiles = (M + BM - 1) / BM;
+  const int w0 = xcd_remap(blockIdx.x, n_tiles * m_tiles * S);  // the grid, from the arguments
   const int split = SPLIT ? w0 % S : 0;
   const int w = SPLIT ? w0 / S : w0;  // tile
   const int nt = w % n_tiles, mt_idx = w / n_tiles;
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(64 * WV, 1) void gemm_int8_medium_kernel(
     // barrier) one lane takes the tile's ticket; the workgroup that draws
     // S - 1 is the last, re-arms the ticket and reads the S partials back
     // with coherent loads, in split order.  Nobody waits on anybody.
-    const int tiles = gridDim.x / S;
+    const int tiles = n_tiles * m_tiles;
     uint32_t* tickets = ws;
     constexpr int NTH = 64 * WV;
     constexpr int PART = MT * NT * NTH;  // 16-byte units per partial

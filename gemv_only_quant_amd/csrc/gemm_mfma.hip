@@ -121,7 +121,10 @@ __device__ __forceinline__ void skinny_body(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, quad = lane >> 4;
   const int S = SPLIT ? splits_of(tile_opts) : 1;
-  const int w0 = xcd_remap(blockIdx.x, gridDim.x);
+  // the grid (tiles x splits), from the arguments: no read of the dispatch's
+  // grid size, which is a memory load at wave start
+  const int m_tiles = (M + 16 * MT - 1) / (16 * MT);
+  const int w0 = xcd_remap(blockIdx.x, n_tiles * m_tiles * S);
   const int split = SPLIT ? w0 % S : 0;
   const int w = SPLIT ? w0 / S : w0;  // tile
   const int nt = w % n_tiles, mt_idx = w / n_tiles;
@@ -349,7 +352,7 @@ __device__ __forceinline__ void skinny_body(
     // the last, and every other partial of its tile is already past the L2s;
     // it re-arms the ticket and reads the S partials back with coherent
     // loads.  Nobody waits on anybody: the workgroups that are not last end.
-    const int tiles = gridDim.x / S;
+    const int tiles = n_tiles * m_tiles;
     uint32_t* tickets = ws;
     float* parts = reinterpret_cast<float*>(ws + ((tiles + 63) & ~63));
     constexpr int PART = ROWS * COLS;  // floats per partial
@@ -407,7 +410,7 @@ template <int W_BIT, int XDT, int GS, int MT, int NT, int DEPTH, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void gemm_skinny_split_kernel(
     const uint16_t* __restrict__ x, const u32x4_t* __restrict__ Qt,
     const void* __restrict__ scales, const uint32_t* __restrict__ qz, void* __restrict__ y,
-    uint32_t* __restrict__ ws, int M, int N, int K, int tile_opts) {
+    int M, int N, int K, int tile_opts, uint32_t* __restrict__ ws) {
   skinny_body<W_BIT, XDT, GS, MT, NT, DEPTH, WAVES, true>(x, Qt, scales, qz, y, ws, M, N, K,
                                                           tile_opts);
 }
@@ -545,8 +548,9 @@ static hipError_t launch_skinny_w(const MatmulArgs& a, const GemmPlan& p) {
     if (p.splits > 1)
       return launch_kernel(gemm_skinny_split_kernel<W_BIT, XDT, GS, MT, NT, DEPTH, WAVES>,
                            dim3((unsigned)(blocks * p.splits)), dim3(64 * WAVES), a.stream, a.x,
-                           a.Q, a.scales, a.zeros, a.y, a.workspace, a.M, a.N, a.K,
-                           pack_tiles(p.n_tiles, a.y_dtype, a.group_mask == 0, p.splits));
+                           a.Q, a.scales, a.zeros, a.y, a.M, a.N, a.K,
+                           pack_tiles(p.n_tiles, a.y_dtype, a.group_mask == 0, p.splits),
+                           static_cast<uint32_t*>(a.workspace));
   }
   return launch_kernel(gemm_skinny_kernel<W_BIT, XDT, GS, MT, NT, DEPTH, WAVES>,
                        dim3((unsigned)blocks), dim3(64 * WAVES), a.stream, a.x, a.Q, a.scales,

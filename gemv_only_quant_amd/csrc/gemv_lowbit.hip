@@ -56,7 +56,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lowbit_kernel(
   const int wave = threadIdx.x >> 6;
   const int cq = lane % CQ;
   const int grp = wave * (64 / CQ) + lane / CQ;
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const int tile = xcd_remap(blockIdx.x, (N + CW - 1) / CW);  // the grid
   const int n0 = tile * CW + cq * 4;
   const bool col_ok = n0 < N;  // N % 4 == 0: the quad is all in or all out
 

@@ -117,7 +117,7 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, oct = lane >> 4;
-  const int s = xcd_remap(blockIdx.x, gridDim.x);
+  const int s = xcd_remap(blockIdx.x, N >> 4);  // the grid: one workgroup per strip
   const int nblk = K / KB;
 
   // one pass in LDS: the x slice (row m at m * PASS_K, as stored), its octet
@@ -412,7 +412,7 @@ template <int W_BIT, int XDT, int MB, int SPB, int NBW, int WV>
 static hipError_t launch_tile_nbw(const MatmulArgs& a) {
   const int gs_opt = a.group_mask == 0 ? -1 : __builtin_ctz((unsigned)a.group_size);
   const int m_ydt = a.M | ((a.y_dtype == YF32 ? 0 : a.y_dtype) << 8);
-  const dim3 grid((unsigned)(a.N / 16)), block(64 * WV);
+  const dim3 grid((unsigned)(a.N >> 4)), block(64 * WV);
   if (a.y_dtype == YF32)
     return launch_kernel(gemv_tile_kernel<W_BIT, XDT, MB, NBW, SPB, true, WV>, grid, block,
                          a.stream, a.x, a.Q, a.scales, a.zeros, a.y, m_ydt, a.N, a.K, gs_opt);

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void i8t2_gemm_kernel(const int8_t* __restrict
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int l16 = lane & 15, quad = lane >> 4;
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int w = xcd_remap(blockIdx.x, n_tiles * ((M + 16 * MT - 1) / (16 * MT)));  // the grid
   const int nt = w % n_tiles, m0 = (w / n_tiles) * 16 * MT;
   const int strips = N / 16, nkb = K / 256;
   const int s0 = (nt * 4 + wave) * NT4;
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(256) void i8t2_skinny_kernel(const int8_t* __restri
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l16 = lane & 15, quad = lane >> 4;
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  const int w = xcd_remap(blockIdx.x, n_tiles);  // the grid: one workgroup per strip
   const int nt = w % n_tiles, m0 = (w / n_tiles) * 16;
   const int strips = N / 16, nkb = K / 256;
   const int s0 = nt * NT;

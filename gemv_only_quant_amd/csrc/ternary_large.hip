@@ -300,7 +300,7 @@ __global__ __launch_bounds__(256, 1) void i8t2_large_kernel(const int8_t* __rest
     i8t2_large_body<4>(x, Wt, y, M, N, K, n_full, 0, b, full, xa);
   else
     i8t2_large_body<3>(x, Wt, y, M, N, K, tail_tiles, 16 * n_full, b - full,
-                       (int)gridDim.x - full, xa);
+                       tail_tiles * m_tiles, xa);
 }
 
 // ---------------------------------------------------------------- host side
