@@ -238,11 +238,10 @@ __global__ __launch_bounds__(64 * WV, 1) void gemm_int8_medium_kernel(
     // barrier) one lane takes the tile's ticket; the workgroup that draws
     // S - 1 is the last, re-arms the ticket and reads the S partials back
     // with coherent loads, in split order.  Nobody waits on anybody.
-    const int tiles = n_tiles * m_tiles;
-    uint32_t* tickets = ws;
+    uint32_t* tickets = ws;  // kTicketSlots of them, then the partial tiles
     constexpr int NTH = 64 * WV;
     constexpr int PART = MT * NT * NTH;  // 16-byte units per partial
-    const buf_t pbuf = make_buf(ws + ((tiles + 63) & ~63) + (size_t)w * S * PART * 4,
+    const buf_t pbuf = make_buf(ws + kTicketSlots + (size_t)w * S * PART * 4,
                                 (uint32_t)(S * PART * 16));
 #pragma unroll
     for (int i = 0; i < MT; ++i)
@@ -283,7 +282,7 @@ constexpr int kMediumDepth = 4;
 
 size_t medium_workspace_bytes(int tiles, int splits, int mt, int strips_per_wg) {
   if (splits <= 1) return 0;
-  return (size_t)((tiles + 63) & ~63) * 4 + (size_t)tiles * splits * mt * strips_per_wg * 64 * 16;
+  return (size_t)kTicketSlots * 4 + (size_t)tiles * splits * mt * strips_per_wg * 64 * 16;
 }
 
 template <int XDT, int MT, int NT, int WV>

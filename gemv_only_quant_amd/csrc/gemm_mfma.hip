@@ -352,9 +352,8 @@ __device__ __forceinline__ void skinny_body(
     // the last, and every other partial of its tile is already past the L2s;
     // it re-arms the ticket and reads the S partials back with coherent
     // loads.  Nobody waits on anybody: the workgroups that are not last end.
-    const int tiles = n_tiles * m_tiles;
-    uint32_t* tickets = ws;
-    float* parts = reinterpret_cast<float*>(ws + ((tiles + 63) & ~63));
+    uint32_t* tickets = ws;  // kTicketSlots of them, then the partial tiles
+    float* parts = reinterpret_cast<float*>(ws + kTicketSlots);
     constexpr int PART = ROWS * COLS;  // floats per partial
     const buf_t pbuf = make_buf(parts + (size_t)w * S * PART, (uint32_t)S * PART * 4u);
     for (int o = 4 * threadIdx.x; o < PART; o += 4 * 64 * WAVES) {
@@ -486,6 +485,7 @@ GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size, bool with_wor
     if (with_workspace)
       while (s < 8 && tiles * (s + 1) <= 248 && nst / (s + 1) >= 4) ++s;
     if (with_workspace && want_med_s >= 1 && want_med_s <= 16) s = want_med_s;
+    if (tiles > kTicketSlots) s = 1;
     if (s > 1 || tiles >= 192) {
       p.kind = 3;
       p.mtile = 16 * mmt;
@@ -526,15 +526,14 @@ GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size, bool with_wor
     while (s > 1 && nst / s < 8) --s;  // 4 waves x 2 stages
     p.splits = s;
   }
-  if (with_workspace && want_s >= 1 && want_s <= 16) p.splits = want_s;
+  if (with_workspace && want_s >= 1 && want_s <= 16 && tiles <= kTicketSlots) p.splits = want_s;
   const bool w8 = nt == 1 && (mt == 1 || (mt == 2 && w_bit != 2));
   p.waves = (p.splits == 1 && tiles < 128 && w8 && nst >= 16) ? 8 : 4;
   static const int want = env_int("QMM_SKINNY_WAVES");
   if (p.splits == 1 && (want == 4 || (want == 8 && w8))) p.waves = want;
   p.workspace_bytes = 0;
   if (p.splits > 1) {
-    const size_t tickets = (size_t)((tiles + 63) & ~63L) * 4;
-    p.workspace_bytes = tickets + (size_t)tiles * p.splits * p.mtile * 16 * nt * 4;
+    p.workspace_bytes = (size_t)kTicketSlots * 4 + (size_t)tiles * p.splits * p.mtile * 16 * nt * 4;
   }
   return p;
 }

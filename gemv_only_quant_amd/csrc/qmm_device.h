@@ -25,9 +25,11 @@ __device__ __forceinline__ void with_y(void* y, int ydt, F&& f);
 
 // Options carried in the top bits of a kernel's tile-count argument, so no
 // kernel needs more than 56 bytes of explicit arguments (64 with a
-// workspace): on this runtime one argument more (a 320-byte instead of a
-// 312-byte argument segment, with the hidden arguments) measured +0.3 us on
-// every launch of a 6 us kernel.
+// workspace, the workspace pointer last): 56 bytes are what the build
+// preloads into SGPRs (14 user SGPRs beside the argument pointer), and one
+// argument more (a 320-byte instead of a 312-byte argument segment, with the
+// hidden arguments) had measured +0.3 us on every launch of a 6 us kernel
+// before arguments were preloaded.
 //   bits 0-23 tile count, bits 24-27 K splits - 1, bits 28-29 output type,
 //   bit 30 per-column scales
 constexpr int kTileBits = 24;

@@ -86,6 +86,13 @@ struct GemmPlan {
   int tail_tiles;  // large-M: narrow 192-column tiles after the full ones (0: none)
   size_t workspace_bytes;  // tickets + partial tiles when splits > 1, else 0
 };
+// Workspace of a plan that splits K over workgroups: kTicketSlots 32-bit
+// arrival tickets (one per tile, the rest unused), then the plan's partial
+// tiles.  The ticket head has one fixed size for every plan, so the partial
+// tiles of one shape never land on the tickets of another and a workspace
+// serves calls of any shapes in sequence; plans split only when their tiles
+// fit in it.
+constexpr int kTicketSlots = 1024;
 // with_workspace: whether the call has a workspace; without one the plan
 // never splits K over workgroups.
 GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size, bool with_workspace = true);
@@ -99,8 +106,9 @@ void large_split(int m_tiles, int strips, int* n_full, int* n_tail);
 hipError_t launch_gemm_large(const MatmulArgs& a, const GemmPlan& p);
 
 // ---- int8 MFMA GEMM at medium M (gemm_medium.hip) --------------------------
-// Workspace of a plan of `tiles` tiles split `splits` ways: tickets, then the
-// partial tiles (mt 16-row tiles x strips_per_wg 16-column strips each).
+// Workspace of a plan of `tiles` tiles split `splits` ways: the ticket head,
+// then the partial tiles (mt 16-row tiles x strips_per_wg 16-column strips
+// each).
 size_t medium_workspace_bytes(int tiles, int splits, int mt, int strips_per_wg);
 hipError_t launch_gemm_medium(const MatmulArgs& a, const GemmPlan& p);
 

@@ -68,13 +68,13 @@ def test_fuzz_gemm(seed, with_ws):
     Qt = qmm.pack(d.Q, case.N, case.K, case.w_bit)
     y = torch.full((case.M, case.N), float("nan"), dtype=torch.float32, device="cuda")
     need = qmm.qmm_workspace_bytes(case.M, case.N, case.K, case.w_bit, case.group_size)
-    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda") if with_ws and need else None
+    ws = torch.zeros(max(need, 4096), dtype=torch.uint8, device="cuda") if with_ws and need else None
     qmm.qmm_gemm(d.x, Qt, d.scales, d.zeros, y, case.M, case.N, case.K, case.w_bit,
                  case.group_size, workspace=ws)
     _check(case, cpu(y))
-    if ws is not None:  # the split left its tickets re-armed (the first 256 bytes
-        # are tickets or their zero padding whatever the plan's tile count)
-        assert int(ws[:256].view(torch.int32).abs().sum()) == 0
+    if ws is not None:  # the split left its tickets re-armed (the workspace
+        # starts with 1024 of them, whatever the plan's tile count)
+        assert int(ws[:4096].view(torch.int32).abs().sum()) == 0
 
 
 @pytest.mark.parametrize("seed", range(16))

@@ -344,24 +344,28 @@ def test_gemm_small_grid_exact_probe_bit_exact(M, N, K, w_bit, gs, plan):
 def test_split_workspace_rearmed_over_calls():
     """One zero-filled workspace through calls of different shapes (different
     tile and split counts): each result is right, and after every call the
-    tickets are back at zero."""
+    tickets are back at zero.  The int8 shape at 16 x 10240 x 1024 has 80
+    tiles (K split 2 ways): its tickets 64-79 lie where a layout that put the
+    partial tiles right after each plan's own tickets would have left the
+    partials of a call with at most 64 tiles."""
     ws = torch.zeros(16 << 20, dtype=torch.uint8, device="cuda")
-    shapes = [(16, 64, 4096, 4, 128), (16, 1024, 14336, 4, 128), (7, 32, 8192, 2, 64),
-              (16, 64, 4096, 4, 128), (40, 48, 4096, 8, 0), (5, 16, 2048, 4, 128)]
+    shapes = [(16, 64, 4096, 4, 128), (16, 1024, 14336, 4, 128), (16, 10240, 1024, 8, 0),
+              (7, 32, 8192, 2, 64), (16, 10240, 1024, 8, 0), (16, 64, 4096, 4, 128),
+              (40, 48, 4096, 8, 0), (5, 16, 2048, 4, 128)]
     for i, (M, N, K, wb, gs) in enumerate(shapes):
         need = qmm.qmm_workspace_bytes(M, N, K, wb, gs)
         assert 0 < need <= ws.numel(), (M, N, K, need)
         case = (si.int8_case(M, N, K, si.BF16, seed=70 + i) if wb == 8 else
                 si.exact_lowbit_case(M, N, K, wb, gs, si.F16, False, seed=70 + i))
+        y_ref, a_ref = oracle.qmm(*case.oracle_args())
         for rep in range(3):
             y = run_gemm(case, ws=ws)
-            y_ref, a_ref = oracle.qmm(*case.oracle_args())
             if wb == 8:
                 assert_within_bound(y, y_ref, a_ref, f"call {i}.{rep}")
             else:
                 assert np.array_equal(y.astype(np.float64), y_ref), f"call {i}.{rep}"
-            # every shape here has <= 64 tiles: its tickets are the first 256 bytes
-            assert int(torch.count_nonzero(ws[:256])) == 0, f"tickets left armed after {i}"
+            # the workspace starts with 1024 tickets (4 KiB), whatever the plan
+            assert int(torch.count_nonzero(ws[:4096])) == 0, f"tickets left armed after {i}"
 
 
 def test_split_undersized_workspace_refused():
