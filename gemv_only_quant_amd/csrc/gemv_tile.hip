@@ -18,11 +18,12 @@
 //    8 c + i, nibble t (t < 4) code 2t and nibble 4 + t code 2t + 1, so
 //    (w >> 4t) & 0x000F000F is the code pair (2t, 2t + 1); int2 the same in
 //    2-bit fields, two 32-k halves per word;
-//  * per pass the loads go out in the order x slice, weights, scales and
-//    zero words; only the x slice gates the dot products (it is shared by
-//    every workgroup and comes from cache), each block then waits for its
-//    own weights alone, and the scales are needed only by the closing group
-//    epilogue (loads complete in order);
+//  * per pass the loads go out in the order x slice, 3/4 of the weights,
+//    scales and zero words, the last weights; only the x slice gates the dot
+//    products (it is shared by every workgroup and comes from cache), each
+//    block then waits for its own weights (and the loads issued before
+//    them: loads complete in order), and the scales are needed only by the
+//    closing group epilogue;
 //  * the x slice goes to LDS unchanged (pairs of consecutive k are already
 //    the dot2 operand pairs), with its per-octet sums;
 //  * codes become (B + q_a, B + q_b) 16-bit pairs (B = 1024 fp16, 128 bf16)
@@ -173,14 +174,21 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
       const int m = q / PO, k = k0 + 8 * (q % PO);
       xr[j] = buf_load128(xbuf, (q < XCH && m < M && k < K) ? (m * K + k) * 2 : OUT);
     }
-    // 2. weights: one 1 KiB block per load instruction
+    // 2. weights: one 1 KiB block per load instruction, the first 3/4 of
+    // them here; then the scales and zero words, then the last quarter of
+    // the weights.  Loads complete in order: the scale and zero loads (which
+    // only the pass's closing epilogue reads) return while the last blocks
+    // still stream in, and their scalar offset arithmetic does not hold back
+    // the first blocks.  Measured at M=1 K=N=4096 int4 g128 (us, same box):
+    // weights 6 / 8 before them 4.69-4.76, 4 / 8 4.74-4.81, all 8 4.86-4.90,
+    // none (scales first) 4.82-4.90.
     const int kb0 = k0 / KB + wave * NBW;        // this wave's first block
+    constexpr int WEARLY = NBW * 3 / 4;
     u32x4_t wq[NBW];
 #pragma unroll
-    for (int i = 0; i < NBW; ++i) wq[i] = buf_load128(qbuf, ((kb0 + i) * 64 + lane) * 16);
+    for (int i = 0; i < WEARLY; ++i) wq[i] = buf_load128(qbuf, ((kb0 + i) * 64 + lane) * 16);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // scales and zero words last: only the pass's closing epilogue reads
-    // them, so no dot product waits for them (loads complete in order)
     uint32_t su[DIRECT ? 1 : SU], zu[DIRECT ? 1 : ZU];
     uint32_t sd[DIRECT ? NBW * SPB : 1], zd[DIRECT ? NBW * SPB : 1];
     if constexpr (DIRECT) {
@@ -205,6 +213,9 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
         zu[j] = buf_load32(zbuf, u < ZR * 16 ? ((zr0 + (u >> 4)) * N + (u & 15)) * 4 : OUT);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = WEARLY; i < NBW; ++i) wq[i] = buf_load128(qbuf, ((kb0 + i) * 64 + lane) * 16);
     // 3. the pass to LDS
     if (k0 > 0) __syncthreads();  // the previous pass is done reading
 #pragma unroll
