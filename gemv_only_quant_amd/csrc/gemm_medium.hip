@@ -138,7 +138,7 @@ __global__ __launch_bounds__(64 * WV, 1) void gemm_int8_medium_kernel(
   };
   auto load_slot = [&](int s, int b, int st, WRegs& R) {
     R.slot[s][b] = __builtin_amdgcn_raw_buffer_load_b128(
-        qb, lane * 16, (s * nblk + 2 * (sa + st) + b) * 1024, 0);
+        qb, lane * 16, (s * nblk + 2 * (sa + st) + b) * 1024, kStream);
   };
   constexpr int NWL = 2 * NT;  // weight slot loads per stage
   auto load_w = [&](int st, WRegs& R) {

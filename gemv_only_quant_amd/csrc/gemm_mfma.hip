@@ -192,7 +192,7 @@ __device__ __forceinline__ void skinny_body(
 #pragma unroll
       for (int b = 0; b < BLK; ++b) {
         const int kb = min(st * BLK + b, nblk - 1);
-        R.w[s][b] = buf_load128(qbuf, ((s * nblk + kb) * 64 + lane) * 16);
+        R.w[s][b] = buf_load128_stream(qbuf, ((s * nblk + kb) * 64 + lane) * 16);
       }
 #pragma unroll
     for (int i = 0; i < MT; ++i)

@@ -75,7 +75,8 @@ __global__ __launch_bounds__(256) void gemv_int8_kernel(
 #pragma unroll
     for (int r = 0; r < RN; ++r)
       q[r] = (kok && n0 + r < N)
-                 ? *reinterpret_cast<const u32x4_t*>(Q + (size_t)(n0 + r) * K + k)
+                 ? __builtin_nontemporal_load(
+                       reinterpret_cast<const u32x4_t*>(Q + (size_t)(n0 + r) * K + k))
                  : u32x4_t{0x80808080u, 0x80808080u, 0x80808080u, 0x80808080u};
     // the rows' scales, loaded behind the first weights (loads return in
     // order): their latency overlaps the weights' instead of following the

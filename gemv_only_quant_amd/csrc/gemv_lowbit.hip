@@ -98,7 +98,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_lowbit_kernel(
     u32x4_t wq[RL];
 #pragma unroll
     for (int i = 0; i < RL; ++i)
-      wq[i] = *reinterpret_cast<const u32x4_t*>(qw + (size_t)(rowc + i) * N + nc);
+      wq[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(qw + (size_t)(rowc + i) * N + nc));
 
     // 3. scale and zero point of the lane's group, for its four columns
     const int g = (rowc * PACK) / group_size;

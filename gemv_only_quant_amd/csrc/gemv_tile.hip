@@ -186,7 +186,7 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
     constexpr int WEARLY = NBW * 3 / 4;
     u32x4_t wq[NBW];
 #pragma unroll
-    for (int i = 0; i < WEARLY; ++i) wq[i] = buf_load128(qbuf, ((kb0 + i) * 64 + lane) * 16);
+    for (int i = 0; i < WEARLY; ++i) wq[i] = buf_load128_stream(qbuf, ((kb0 + i) * 64 + lane) * 16);
     __builtin_amdgcn_sched_barrier(0);
 
     uint32_t su[DIRECT ? 1 : SU], zu[DIRECT ? 1 : ZU];
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = WEARLY; i < NBW; ++i) wq[i] = buf_load128(qbuf, ((kb0 + i) * 64 + lane) * 16);
+    for (int i = WEARLY; i < NBW; ++i) wq[i] = buf_load128_stream(qbuf, ((kb0 + i) * 64 + lane) * 16);
     // 3. the pass to LDS
     if (k0 > 0) __syncthreads();  // the previous pass is done reading
 #pragma unroll

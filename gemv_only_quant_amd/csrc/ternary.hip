@@ -287,7 +287,8 @@ __global__ __launch_bounds__(256) void i8t2_skinny_kernel(const int8_t* __restri
     for (int d = 0; d < DEPTH; ++d) {
       const int k = min(kb + d, kb1 - 1);  // past the range: re-read, not used
 #pragma unroll
-      for (int s = 0; s < NT; ++s) wr[d][s] = Wt[((size_t)sidx[s] * nkb + k) * 64 + lane];
+      for (int s = 0; s < NT; ++s)
+        wr[d][s] = __builtin_nontemporal_load(&Wt[((size_t)sidx[s] * nkb + k) * 64 + lane]);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         xr[d][j] = *reinterpret_cast<const u32x4_t*>(xrows[j] + (size_t)k * 256);
