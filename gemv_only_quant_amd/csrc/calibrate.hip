@@ -66,7 +66,8 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(const u32x4_t* __restric
 // load (the GEMV's recipe: per 32-bit word one shift, four mask-ors under
 // the fp16 1024 pattern, four v_dot2c_f32_f16 against x from LDS); bit 2
 // the GEMV's closing step (every lane's partial to LDS, a barrier, 16
-// threads adding 16 values each).  Without bit 2 every thread stores one
+// threads adding 16 values each).  The weight loads carry the GEMV's
+// non-temporal hint.  Without bit 2 every thread stores one
 // word.  Reads src[0 .. gridDim.x * 32 KiB), x[0 .. 8 KiB); writes dst[0 ..
 // gridDim.x * 256) words.
 template <int V>
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(256) void readonly_probe_kernel(const u32x4_t* __re
   }
   u32x4_t v[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = buf_load128(b, ((wave * 8 + i) * 64 + lane) * 16);
+  for (int i = 0; i < 8; ++i) v[i] = buf_load128_stream(b, ((wave * 8 + i) * 64 + lane) * 16);
   if constexpr (XS) {
     xs[threadIdx.x] = xr[0];
     xs[threadIdx.x + 256] = xr[1];

@@ -473,8 +473,8 @@ hipError_t launch_gemv_tile(const MatmulArgs& a) {
 #ifdef QMM_PHASE_STAMPS
 // The reference the stamps are read against: the same grid (one 256-thread
 // workgroup per 16-column strip), each workgroup reading its strip's
-// nblk KiB in 1 KiB wave loads, 8 per wave in flight, summing and storing
-// one value per lane.  Slots: 0 entry, 3 last load returned, 5 stored.
+// nblk KiB in 1 KiB wave loads (with the GEMV's non-temporal hint), 8 per
+// wave in flight, summing and storing one value per lane.  Slots: 0 entry, 3 last load returned, 5 stored.
 __global__ __launch_bounds__(256) void phase_readonly_kernel(const u32x4_t* __restrict__ src,
                                                              uint32_t* __restrict__ dst,
                                                              int nblk) {
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(256) void phase_readonly_kernel(const u32x4_t* __re
   for (int kb = wave * 8; kb < nblk; kb += 32) {
     u32x4_t v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = buf_load128(b, ((kb + i) * 64 + lane) * 16);
+    for (int i = 0; i < 8; ++i) v[i] = buf_load128_stream(b, ((kb + i) * 64 + lane) * 16);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc += v[i][0] ^ v[i][1] ^ v[i][2] ^ v[i][3];
   }
