@@ -33,7 +33,7 @@
 //    where the column-wide term (B + z) sum x comes from a per-pass table of
 //    group sums of x and is taken by one of the column's four k-octet lanes;
 //    the group scale multiplies once;
-//  * the 4 lanes of a column meet through two cross-lane adds, the 4 waves
+//  * the 4 lanes of a column meet through two lane swaps, the 4 waves
 //    through LDS.
 // Measured (graph-replayed, 64 weight copies; M=1 K=N=4096 int4 g128 fp16):
 // weight loads alone 3.4 us, the whole kernel 4.6 us against 4.8 for the
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
   constexpr bool DIRECT = NBW * SPB <= 8;
   __shared__ uint16_t sl[DIRECT ? 1 : GPP * 16];
   __shared__ uint32_t zl[DIRECT ? 1 : ZR * 16];
-  __shared__ float red[WV][4][MB][16];  // per wave and k-octet lane group
+  __shared__ float red[WV][MB][16];  // per wave: its columns' sums
 
   // descriptors: a block past the strip, a row past M, a group past G read 0
   const buf_t qbuf = make_buf(Qt + (size_t)s * nblk * 64, (uint32_t)nblk * 1024u);
@@ -390,10 +390,27 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
     }
   }
 
-  // 7. every lane's partial to LDS; one thread per output adds the column's
-  // 4 k-octet lanes of every wave (one LDS round trip, no shuffles)
+  // 7. the column's 4 k-octet lanes (the same lane of the wave's 4 rows of
+  // 16) meet by two lane swaps: v_permlane16_swap trades rows 1 and 2 of
+  // its two operands' row pairs, v_permlane32_swap their upper and lower
+  // halves, so adding both results of each leaves every lane with its
+  // column's sum over the 4 rows.  Then the waves meet in LDS, and one
+  // thread per output adds them.
+  // (Written as asm: this compiler's builtins for the two swaps hand back
+  // the first register for both results.  The s_nop covers the hazard of a
+  // swap reading a register a VALU instruction has just written.)
 #pragma unroll
-  for (int m = 0; m < MB; ++m) red[wave][oct][m][col] = r[m];
+  for (int m = 0; m < MB; ++m) {
+    float a0 = r[m], a1 = r[m];
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a0), "+v"(a1));
+    float c0 = a0 + a1, c1 = c0;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(c0), "+v"(c1));
+    r[m] = c0 + c1;
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int m = 0; m < MB; ++m) red[wave][m][col] = r[m];
+  }
   __syncthreads();
   auto store = [&](auto* yt) {
     using T = typename std::remove_pointer<decltype(yt)>::type;
@@ -402,9 +419,7 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
       if (m < M) {
         float sum = 0.f;
 #pragma unroll
-        for (int v = 0; v < WV; ++v)
-#pragma unroll
-          for (int o = 0; o < 4; ++o) sum += red[v][o][m][c];
+        for (int v = 0; v < WV; ++v) sum += red[v][m][c];
         yt[(size_t)m * N + 16 * s + c] = (T)sum;
       }
     }
