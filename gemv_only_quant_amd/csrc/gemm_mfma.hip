@@ -344,8 +344,8 @@ __device__ __forceinline__ void skinny_body(
       }
     });
   } else {
-    // Workspace: one ticket per tile (zero between calls), padded to 256
-    // bytes, then S partial tiles of ROWS x COLS fp32 per tile.  The partial
+    // Workspace: the first kTicketSlots words hold one ticket per tile (zero
+    // between calls), then S partial tiles of ROWS x COLS fp32 per tile.  The partial
     // goes out with coherent stores; once they have completed (vmcnt 0 in
     // every wave, then the barrier) one lane takes the tile's ticket.  The
     // ticket is an agent-scope atomic, so whichever workgroup draws S - 1 is

@@ -35,9 +35,10 @@
 //    the group scale multiplies once;
 //  * the 4 lanes of a column meet through two lane swaps, the 4 waves
 //    through LDS.
-// Measured (graph-replayed, 64 weight copies; M=1 K=N=4096 int4 g128 fp16):
-// weight loads alone 3.4 us, the whole kernel 4.6 us against 4.8 for the
-// canonical-layout GEMV on the same box.
+// Measured (graph-replayed over > 512 MB of weight copies, 50 calls per
+// replay; M=1 K=N=4096 int4 g128 fp16): a kernel of the same grid that only
+// loads the weights 3.1 us, this one 3.9 us (3.7 in 2000-call replays),
+// against 4.5 for the canonical-layout GEMV on the same box.
 #include <type_traits>
 
 #include "qmm_device.h"
@@ -179,9 +180,9 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
     // the weights.  Loads complete in order: the scale and zero loads (which
     // only the pass's closing epilogue reads) return while the last blocks
     // still stream in, and their scalar offset arithmetic does not hold back
-    // the first blocks.  Measured at M=1 K=N=4096 int4 g128 (us, same box):
-    // weights 6 / 8 before them 4.69-4.76, 4 / 8 4.74-4.81, all 8 4.86-4.90,
-    // none (scales first) 4.82-4.90.
+    // the first blocks.  Measured at M=1 K=N=4096 int4 g128 (us, same box,
+    // before the non-temporal hint): weights 6 / 8 before them 4.69-4.76,
+    // 4 / 8 4.74-4.81, all 8 4.86-4.90, none (scales first) 4.82-4.90.
     const int kb0 = k0 / KB + wave * NBW;        // this wave's first block
     constexpr int WEARLY = NBW * 3 / 4;
     u32x4_t wq[NBW];
@@ -391,11 +392,13 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
   }
 
   // 7. the column's 4 k-octet lanes (the same lane of the wave's 4 rows of
-  // 16) meet by two lane swaps: v_permlane16_swap trades rows 1 and 2 of
-  // its two operands' row pairs, v_permlane32_swap their upper and lower
-  // halves, so adding both results of each leaves every lane with its
-  // column's sum over the 4 rows.  Then the waves meet in LDS, and one
-  // thread per output adds them.
+  // 16) meet by two lane swaps.  v_permlane16_swap exchanges the odd rows of
+  // its first operand with the even rows of its second: with both holding
+  // r, their sum is r(row 0) + r(row 1) in rows 0-1 and r(2) + r(3) in rows
+  // 2-3.  v_permlane32_swap exchanges the upper half of the first with the
+  // lower half of the second: the sum of both is then the 4 rows' total in
+  // every lane.  Then the waves meet in LDS, and one thread per output adds
+  // them.
   // (Written as asm: this compiler's builtins for the two swaps hand back
   // the first register for both results.  The s_nop covers the hazard of a
   // swap reading a register a VALU instruction has just written.)
@@ -489,7 +492,8 @@ hipError_t launch_gemv_tile(const MatmulArgs& a) {
 // The reference the stamps are read against: the same grid (one 256-thread
 // workgroup per 16-column strip), each workgroup reading its strip's
 // nblk KiB in 1 KiB wave loads (with the GEMV's non-temporal hint), 8 per
-// wave in flight, summing and storing one value per lane.  Slots: 0 entry, 3 last load returned, 5 stored.
+// wave in flight, summing and storing one value per lane.  Slots: 0 entry,
+// 3 last load returned, 5 stored.
 __global__ __launch_bounds__(256) void phase_readonly_kernel(const u32x4_t* __restrict__ src,
                                                              uint32_t* __restrict__ dst,
                                                              int nblk) {

@@ -120,13 +120,15 @@ __device__ __forceinline__ u32x4_t buf_load128(buf_t b, int off) {
   return __builtin_amdgcn_raw_buffer_load_b128(b, off, 0, 0);
 }
 // Weights that a call reads exactly once go through the caches with the
-// non-temporal hint (the `nt` cache-policy bit): the lines are not kept for
-// reuse, so a stream of them does not displace x, the scales or other
-// workgroups' lines.  Measured on the headline GEMV (M=1 K=N=4096 int4 g128,
-// weights rotated over > 512 MB): 4.72-4.75 -> 3.99-4.04 us per call in
-// 50-call graph replays; the int4 M=16 and small-N skinny GEMMs 3% faster.
-// (A model whose weights would stay in the 256 MB Infinity Cache from one
-// call to the next gives that reuse up.)
+// non-temporal hint (the `nt` cache-policy bit): their lines are not
+// allocated for reuse, so the caches need not make room for them.  Measured
+// on the headline GEMV (M=1 K=N=4096 int4 g128, weights rotated over > 512
+// MB, replays after a cache-evicting pass): 4.72-4.75 -> 3.99-4.04 us per
+// call in 50-call graph replays, unchanged in 2000-call ones; the int8
+// medium GEMMs 4-10% and the int4 skinny ones 3% faster.  (A model whose
+// weights would stay in the 256 MB Infinity Cache from one call to the next
+// gives that reuse up; the prefill, which re-reads each weight tile once per
+// row tile, keeps the default policy: with the hint it measured 3-8% slower.)
 constexpr int kStream = 2;  // nt
 __device__ __forceinline__ u32x4_t buf_load128_stream(buf_t b, int off) {
   return __builtin_amdgcn_raw_buffer_load_b128(b, off, 0, kStream);
