@@ -392,24 +392,10 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
   }
 
   // 7. the column's 4 k-octet lanes (the same lane of the wave's 4 rows of
-  // 16) meet by two lane swaps.  v_permlane16_swap exchanges the odd rows of
-  // its first operand with the even rows of its second: with both holding
-  // r, their sum is r(row 0) + r(row 1) in rows 0-1 and r(2) + r(3) in rows
-  // 2-3.  v_permlane32_swap exchanges the upper half of the first with the
-  // lower half of the second: the sum of both is then the 4 rows' total in
-  // every lane.  Then the waves meet in LDS, and one thread per output adds
-  // them.
-  // (Written as asm: this compiler's builtins for the two swaps hand back
-  // the first register for both results.  The s_nop covers the hazard of a
-  // swap reading a register a VALU instruction has just written.)
+  // 16) meet by two lane swaps (rows4_sum); then the waves meet in LDS, and
+  // one thread per output adds them.
 #pragma unroll
-  for (int m = 0; m < MB; ++m) {
-    float a0 = r[m], a1 = r[m];
-    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a0), "+v"(a1));
-    float c0 = a0 + a1, c1 = c0;
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(c0), "+v"(c1));
-    r[m] = c0 + c1;
-  }
+  for (int m = 0; m < MB; ++m) r[m] = rows4_sum(r[m]);
   if (lane < 16) {
 #pragma unroll
     for (int m = 0; m < MB; ++m) red[wave][m][col] = r[m];

@@ -96,6 +96,24 @@ __device__ __forceinline__ float dpp_add(float v) {
                  0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
 }
 
+// Sum over the wave's 4 rows of 16 lanes at each lane position (lane l gets
+// v(l % 16) + v(16 + l % 16) + v(32 + l % 16) + v(48 + l % 16)) by two lane
+// swaps.  v_permlane16_swap exchanges the odd rows of its first operand with
+// the even rows of its second: with both holding v, their sum is v(row 0) +
+// v(row 1) in rows 0-1 and v(2) + v(3) in rows 2-3.  v_permlane32_swap
+// exchanges the upper half of the first with the lower half of the second:
+// the sum of both is then the 4 rows' total in every lane.  Written as asm:
+// this compiler's builtins for the two swaps hand back the first register
+// for both results.  The s_nop covers the hazard of a swap reading a
+// register a VALU instruction has just written.
+__device__ __forceinline__ float rows4_sum(float v) {
+  float a0 = v, a1 = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a0), "+v"(a1));
+  float c0 = a0 + a1, c1 = c0;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(c0), "+v"(c1));
+  return c0 + c1;
+}
+
 // Full-wave sum with DPP: butterfly inside each row of 16 lanes, then the
 // row_bcast steps fold the four rows into lane 63, which is read back.
 __device__ __forceinline__ float wave_sum(float v) {
