@@ -349,9 +349,10 @@ __device__ __forceinline__ void skinny_body(
     // goes out with coherent stores; once they have completed (vmcnt 0 in
     // every wave, then the barrier) one lane takes the tile's ticket.  The
     // ticket is an agent-scope atomic, so whichever workgroup draws S - 1 is
-    // the last, and every other partial of its tile is already past the L2s;
-    // it re-arms the ticket and reads the S partials back with coherent
-    // loads.  Nobody waits on anybody: the workgroups that are not last end.
+    // the last, and every other partial of its tile is already written
+    // through; it re-arms the ticket and reads the S partials back (from its
+    // XCD's L2 when all splits ran there, else with coherent loads).  Nobody
+    // waits on anybody: the workgroups that are not last end.
     uint32_t* tickets = ws;  // kTicketSlots of them, then the partial tiles
     float* parts = reinterpret_cast<float*>(ws + kTicketSlots);
     constexpr int PART = ROWS * COLS;  // floats per partial
@@ -369,22 +370,42 @@ __device__ __forceinline__ void skinny_body(
       buf_store128_coherent(v, pbuf, (split * PART + o) * 4);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __shared__ int last;
+    // The ticket counts arrivals per XCD (ticket_arrivals).  When every
+    // split of the tile ran on this workgroup's XCD, their write-through
+    // stores are in this XCD's L2 and the partials are read from it;
+    // otherwise from past the L2s.
+    const uint32_t xcc = xcc_id();
+    __shared__ int last, local;
     __syncthreads();
     if (threadIdx.x == 0) {
-      const uint32_t ticket =
-          __hip_atomic_fetch_add(tickets + w, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last = ticket == (uint32_t)(S - 1);
+      const uint32_t ticket = __hip_atomic_fetch_add(tickets + w, 1u << (4 * xcc), __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t n = ticket_arrivals(ticket);
+      last = n == (uint32_t)(S - 1);
+      local = ((ticket >> (4 * xcc)) & 15u) == n;
       if (last) __hip_atomic_store(tickets + w, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     if (!last) return;
+    const bool here = local != 0;
     with_y(y, ydt, [&](auto* yt) {
       using T = typename std::remove_pointer<decltype(yt)>::type;
       for (int o = 4 * threadIdx.x; o < PART; o += 4 * 64 * WAVES) {
+        // all S loads in flight at once, then added in split order
+        u32x4_t pv[kMaxSplits];
+        if (here) {
+#pragma unroll
+          for (int q = 0; q < kMaxSplits; ++q)
+            if (q < S) pv[q] = buf_load128_xcd(pbuf, (q * PART + o) * 4);
+        } else {
+#pragma unroll
+          for (int q = 0; q < kMaxSplits; ++q)
+            if (q < S) pv[q] = buf_load128_coherent(pbuf, (q * PART + o) * 4);
+        }
         f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
-        for (int q = 0; q < S; ++q)
-          sum += __builtin_bit_cast(f32x4_t, buf_load128_coherent(pbuf, (q * PART + o) * 4));
+#pragma unroll
+        for (int q = 0; q < kMaxSplits; ++q)
+          if (q < S) sum += __builtin_bit_cast(f32x4_t, pv[q]);
         const int rr = o / COLS, cc = o % COLS;
         const int m = m0 + rr, n = 16 * s0 + cc;
         if (m < M && n < N) {
@@ -526,7 +547,8 @@ GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size, bool with_wor
     while (s > 1 && nst / s < 8) --s;  // 4 waves x 2 stages
     p.splits = s;
   }
-  if (with_workspace && want_s >= 1 && want_s <= 16 && tiles <= kTicketSlots) p.splits = want_s;
+  if (with_workspace && want_s >= 1 && want_s <= kMaxSplits && tiles <= kTicketSlots)
+    p.splits = want_s;
   const bool w8 = nt == 1 && (mt == 1 || (mt == 2 && w_bit != 2));
   p.waves = (p.splits == 1 && tiles < 128 && w8 && nst >= 16) ? 8 : 4;
   static const int want = env_int("QMM_SKINNY_WAVES");

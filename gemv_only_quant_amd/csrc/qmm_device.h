@@ -170,6 +170,29 @@ __device__ __forceinline__ void buf_store128_coherent(u32x4_t v, buf_t b, int of
 __device__ __forceinline__ u32x4_t buf_load128_coherent(buf_t b, int off) {
   return __builtin_amdgcn_raw_buffer_load_b128(b, off, 0, kCoherent);
 }
+// A load that misses this CU's L1 but may hit this XCD's L2 (the sc0 bit):
+// coherent with stores that other CUs of the same XCD wrote through.
+__device__ __forceinline__ u32x4_t buf_load128_xcd(buf_t b, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(b, off, 0, 1);
+}
+// The XCD (accelerator complex die) this wave runs on, 0-7 (a hardware
+// register read).
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  return x & 7u;
+}
+// Arrival ticket of a K-split tile: each workgroup adds one to the 4-bit
+// count of its own XCD (bits 4x .. 4x + 3 for XCD x), so the value before
+// an add tells both how many arrived (the sum of the counts) and whether
+// they all ran on one XCD (one count holds it all).  At most 15 earlier
+// arrivals.
+__device__ __forceinline__ uint32_t ticket_arrivals(uint32_t t) {
+  uint32_t n = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) n += (t >> (4 * i)) & 15u;
+  return n;
+}
 
 // Work-item remap so that consecutive work ids land on one XCD: the
 // dispatcher deals workgroups round-robin over the 8 XCDs, so block b runs

@@ -93,6 +93,9 @@ struct GemmPlan {
 // serves calls of any shapes in sequence; plans split only when their tiles
 // fit in it.
 constexpr int kTicketSlots = 1024;
+// Most workgroups a tile's K is split over (the ticket counts at most 15
+// earlier arrivals per XCD; the last workgroup reads every partial at once).
+constexpr int kMaxSplits = 16;
 // with_workspace: whether the call has a workspace; without one the plan
 // never splits K over workgroups.
 GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size, bool with_workspace = true);
