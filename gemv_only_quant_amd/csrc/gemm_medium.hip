@@ -231,8 +231,8 @@ __global__ __launch_bounds__(64 * WV, 1) void gemm_int8_medium_kernel(
   if constexpr (!SPLIT) {
     store_y(acc);
   } else {
-    // Workspace: one ticket per tile (zero between calls), padded to 256
-    // bytes, then S partial tiles per tile, each 256 lanes x MT NT x 16
+    // Workspace: the first kTicketSlots words hold one ticket per tile (zero
+    // between calls), then S partial tiles per tile, each 256 lanes x MT NT x 16
     // bytes in the accumulator layout.  The partial goes out with coherent
     // stores; once they have completed (vmcnt 0 in every wave, then the
     // barrier) one lane takes the tile's ticket; the workgroup that draws

@@ -505,7 +505,7 @@ GemmPlan plan_gemm(int M, int N, int K, int w_bit, int group_size, bool with_wor
     int s = 1;
     if (with_workspace)
       while (s < 8 && tiles * (s + 1) <= 248 && nst / (s + 1) >= 4) ++s;
-    if (with_workspace && want_med_s >= 1 && want_med_s <= 16) s = want_med_s;
+    if (with_workspace && want_med_s >= 1 && want_med_s <= kMaxSplits) s = want_med_s;
     if (tiles > kTicketSlots) s = 1;
     if (s > 1 || tiles >= 192) {
       p.kind = 3;
