@@ -368,6 +368,26 @@ def test_split_workspace_rearmed_over_calls():
             assert int(torch.count_nonzero(ws[:4096])) == 0, f"tickets left armed after {i}"
 
 
+@pytest.mark.parametrize("N", [48, 128])
+def test_split_read_back_both_paths(N):
+    """The last workgroup of a K-split tile reads the partials from its own
+    XCD's L2 when the ticket shows every split ran there, else past the L2s.
+    N=128: 8 tiles x 4 splits, 32 workgroups remapped so that a tile's splits
+    share an XCD; N=48: 3 tiles x 4 splits, 12 workgroups (not a multiple of
+    8, so no remap), a tile's splits on different XCDs.  Both exact against
+    the oracle, twice on one workspace."""
+    M, K = 16, 4096
+    need = qmm.qmm_workspace_bytes(M, N, K, 4, 128)
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    case = si.exact_lowbit_case(M, N, K, 4, 128, si.F16, False, seed=90 + N)
+    y_ref, _ = oracle.qmm(*case.oracle_args())
+    for rep in range(2):
+        y = run_gemm(case, ws=ws)
+        assert np.array_equal(y.astype(np.float64), y_ref), f"call {rep}"
+        assert int(torch.count_nonzero(ws[:4096])) == 0
+
+
 def test_split_undersized_workspace_refused():
     M, N, K = 16, 64, 4096
     need = qmm.qmm_workspace_bytes(M, N, K, 4, 128)
