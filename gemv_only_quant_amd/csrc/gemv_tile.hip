@@ -18,8 +18,8 @@
 //    8 c + i, nibble t (t < 4) code 2t and nibble 4 + t code 2t + 1, so
 //    (w >> 4t) & 0x000F000F is the code pair (2t, 2t + 1); int2 the same in
 //    2-bit fields, two 32-k halves per word;
-//  * per pass the loads go out in the order x slice, 3/4 of the weights,
-//    scales and zero words, the last weights; only the x slice gates the dot
+//  * per pass the loads go out in the order x slice, 3/8 of the weights,
+//    scales and zero words, the other weights; only the x slice gates the dot
 //    products (it is shared by every workgroup and comes from cache), each
 //    block then waits for its own weights (and the loads issued before
 //    them: loads complete in order), and the scales are needed only by the
@@ -175,16 +175,17 @@ __global__ __launch_bounds__(64 * WV) void gemv_tile_kernel(
       const int m = q / PO, k = k0 + 8 * (q % PO);
       xr[j] = buf_load128(xbuf, (q < XCH && m < M && k < K) ? (m * K + k) * 2 : OUT);
     }
-    // 2. weights: one 1 KiB block per load instruction, the first 3/4 of
-    // them here; then the scales and zero words, then the last quarter of
-    // the weights.  Loads complete in order: the scale and zero loads (which
-    // only the pass's closing epilogue reads) return while the last blocks
+    // 2. weights: one 1 KiB block per load instruction, the first 3/8 of
+    // them here; then the scales and zero words, then the rest of the
+    // weights.  Loads complete in order: the scale and zero loads (which
+    // only the pass's closing epilogue reads) return while the later blocks
     // still stream in, and their scalar offset arithmetic does not hold back
-    // the first blocks.  Measured at M=1 K=N=4096 int4 g128 (us, same box,
-    // before the non-temporal hint): weights 6 / 8 before them 4.69-4.76,
-    // 4 / 8 4.74-4.81, all 8 4.86-4.90, none (scales first) 4.82-4.90.
+    // the first blocks.  Measured at M=1 K=N=4096 int4 g128 with the weights
+    // streamed (us per call, 2000-call replays, same box): weights 3 / 8
+    // before them 3.656-3.657, 2 / 8 3.675-3.681, 4 / 8 3.652-3.668, 5 / 8
+    // 3.665-3.679, 6 / 8 3.687-3.713, 7 / 8 3.82, all 8 3.94.
     const int kb0 = k0 / KB + wave * NBW;        // this wave's first block
-    constexpr int WEARLY = NBW * 3 / 4;
+    constexpr int WEARLY = NBW * 3 / 8;
     u32x4_t wq[NBW];
 #pragma unroll
     for (int i = 0; i < WEARLY; ++i) wq[i] = buf_load128_stream(qbuf, ((kb0 + i) * 64 + lane) * 16);
